@@ -1,0 +1,151 @@
+/*
+ * swin_wmsa.h -- C ABI of the gfx950 (MI355X) shifted-window multi-head
+ * self-attention block forward (Swin V1 and V2).
+ *
+ * Every tensor pointer is a DEVICE pointer to a dense row-major array, unless
+ * stated otherwise.  The caller owns every buffer (inputs, outputs and the
+ * workspace); the library allocates no memory and keeps no state between calls,
+ * so calls are reentrant and thread-safe.  `stream` is a hipStream_t passed as
+ * void* (NULL = the null stream); every call only enqueues work on it and never
+ * synchronises.  Arguments are validated on the host before anything is
+ * launched: an invalid call returns its status code and enqueues nothing.  A
+ * launch failure reported by the HIP runtime returns SWIN_ERR_HIP.  No C++
+ * exception crosses this interface.
+ *
+ * Geometry used throughout:
+ *   x    [B, H, W, C] tokens, channels last.
+ *   M    window side; a window holds N = M*M tokens; nW = (H/M)*(W/M) windows per
+ *        image.  Requires H % M == 0 and W % M == 0.
+ *   s    cyclic shift, 0 <= s < M.  Shifted-frame position (y', x') holds
+ *        original position ((y'+s) mod H, (x'+s) mod W).
+ *   Window w = b*nW + wy*(W/M) + wx; in-window token t = ty*M + tx; window
+ *   slot (w, t) holds shifted-frame position (wy*M+ty, wx*M+tx).
+ */
+#ifndef SWIN_WMSA_H
+#define SWIN_WMSA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SWIN_WMSA_ABI_VERSION 1
+
+typedef enum {
+  SWIN_OK = 0,
+  SWIN_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  SWIN_ERR_SHAPE = 2,       /* sizes inconsistent (H % M, W % M, s range, C % heads) */
+  SWIN_ERR_DTYPE = 3,       /* unknown dtype or mode value                         */
+  SWIN_ERR_UNSUPPORTED = 4, /* valid but not implemented (head dim != 32, M > 32)   */
+  SWIN_ERR_ALIAS = 5,       /* an output overlaps an input or the workspace        */
+  SWIN_ERR_WORKSPACE = 6,   /* workspace smaller than swin_wmsa_workspace_size()   */
+  SWIN_ERR_ALIGN = 7,       /* a pointer is not 16-byte aligned                    */
+  SWIN_ERR_HIP = 8          /* the HIP runtime reported an error at launch         */
+} swin_status;
+
+typedef enum { SWIN_F32 = 0, SWIN_F16 = 1, SWIN_BF16 = 2 } swin_dtype;
+typedef enum { SWIN_V1 = 1, SWIN_V2 = 2 } swin_mode;
+
+typedef struct {
+  int B, H, W, C, heads, M, s;
+  int mode;      /* swin_mode                                                  */
+  int dtype;     /* swin_dtype of x, y, the weights and the linear biases      */
+  float scale;   /* V1 logit multiplier; <= 0 selects (C/heads)^-1/2           */
+  float tau_min; /* V2 lower clip of tau; <= 0 selects 0.01                    */
+} swin_wmsa_desc;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* swin_status_str(swin_status s);
+
+/* SWIN_WMSA_ABI_VERSION of the built library. */
+int swin_abi_version(void);
+
+/*
+ * Cyclic shift + window partition ("Boosting Swin Transformer Speed:
+ * Profiling, Mixed Precision, and Kernel Fusion Secrets", Training Optimization:
+ * window partition / shift are index-mapping operations).
+ *   x  [B, H, W, C]        input, element type dt (only its size matters).
+ *   xw [B*nW, M*M, C]      output; xw[w, t, :] = x[b, (wy*M+ty+s) mod H,
+ *                          (wx*M+tx+s) mod W, :].  A bit-exact permutation.
+ * xw must not overlap x (SWIN_ERR_ALIAS).  B == 0 is a no-op.
+ */
+swin_status swin_partition_shift(const void* x, void* xw, int B, int H, int W, int C,
+                                 int M, int s, swin_dtype dt, void* stream);
+
+/*
+ * Window reverse + inverse shift, the exact inverse of swin_partition_shift
+ * (same page and section).  xw [B*nW, M*M, C] -> x [B, H, W, C].
+ */
+swin_status swin_reverse_unshift(const void* xw, void* x, int B, int H, int W, int C,
+                                 int M, int s, swin_dtype dt, void* stream);
+
+/*
+ * V2 continuous position bias table ("Swin Transformer V2" research summary,
+ * How It Works: a meta-network on log-spaced relative coordinates outputs the
+ * bias).  For every offset (dy, dx) in [-(M-1), M-1]^2, row r = (dy+M-1)*(2M-1)
+ * + (dx+M-1):
+ *   u = coord_scale * (dy, dx)          (coord_scale <= 0 selects 8/(M-1))
+ *   g = sign(u) * log2(1 + |u|) / 3     (per component; log2(8) = 3)
+ *   table[r, h] = 16 * sigmoid( w2[h, :] . relu(w1 g + b1) + b2[h] )
+ *   w1 [hidden, 2] (columns dy, dx), b1 [hidden], w2 [heads, hidden],
+ *   b2 [heads] or NULL (no second bias); table [(2M-1)^2, heads].  All float32.
+ * hidden in 1..4096, heads in 1..64, M in 1..32.
+ */
+swin_status swin_cpb_table(const float* w1, const float* b1, const float* w2,
+                           const float* b2, int hidden, int heads, int M,
+                           float coord_scale, float* table, void* stream);
+
+/*
+ * Workspace bytes swin_wmsa_fwd needs for this descriptor (0 for an invalid
+ * descriptor or B == 0).  The workspace holds per-window intermediates (Q, K,
+ * V and the attention output), is overwritten by every call and must not be
+ * shared by calls that may run concurrently.
+ */
+size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d);
+
+/*
+ * Shifted-window multi-head self-attention block forward (attention sub-layer
+ * only: no LayerNorm, residual or MLP).
+ *   Pages: "Boosting Swin Transformer Speed" -- Introduction (windowed
+ *   attention with shifted windows), Training / Inference Optimization (index
+ *   maps, QKV GEMM + bias + softmax fused, no transposes); "Boost Vision
+ *   Transformer with GPU-Friendly Sparsity and Quantization" -- Section 3.2 and
+ *   Figure 3 (Q/K/V and output projections are GEMMs); "Swin Transformer V2"
+ *   summary -- How It Works (V1 relative position bias, V2 scaled cosine
+ *   attention with tau clipped at 0.01 plus bias B_ij).
+ *
+ *   x       [B, H, W, C]   input tokens, desc->dtype.
+ *   w_qkv   [3C, C]        rows 0..C-1 = q, C..2C-1 = k, 2C..3C-1 = v (out x in);
+ *                          head h uses rows h*d..h*d+d-1 of each block, d = C/heads.
+ *   b_qkv   [3C] or NULL   (NULL = zeros).
+ *   w_proj  [C, C], b_proj [C] or NULL.
+ *   bias_table [(2M-1)^2, heads] float32: V1 learned table or V2 CPB table;
+ *           query i, key j of a window read row (ty_i-ty_j+M-1)*(2M-1) +
+ *           (tx_i-tx_j+M-1).
+ *   tau     [heads] float32, V2 only (raw; max(tau, tau_min) is used); may be
+ *           NULL in V1.
+ *   y       [B, H, W, C]   output, desc->dtype; must not overlap x or the
+ *           workspace.
+ *   workspace, ws_bytes    at least swin_wmsa_workspace_size(desc) bytes.
+ * Per window, with q, k, v the projections of the window's tokens:
+ *   V1: logit(i,j) = scale * q_h(i).k_h(j) + table[idx(i,j), h]
+ *   V2: logit(i,j) = cos(q_h(i), k_h(j)) / max(tau_h, tau_min) + table[idx(i,j), h]
+ *   with s > 0, pairs whose shifted-frame region labels differ get weight 0
+ *   (along an axis of length L: slice 0 for v < L-M, 1 for v < L-s, else 2;
+ *   label = 3*slice_y + slice_x); softmax over the remaining keys; head outputs
+ *   concatenated, projected, and written back at the un-shifted position.
+ * Computes in float32 for SWIN_F32; for SWIN_F16 / SWIN_BF16 the products run on
+ * 16-bit matrix cores with float32 accumulation and float32 softmax.
+ * Requires C/heads == 32 and M <= 32 (else SWIN_ERR_UNSUPPORTED).
+ */
+swin_status swin_wmsa_fwd(const swin_wmsa_desc* desc, const void* x, const void* w_qkv,
+                          const void* b_qkv, const void* w_proj, const void* b_proj,
+                          const float* bias_table, const float* tau, void* y,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIN_WMSA_H */

@@ -1,0 +1,156 @@
+"""Python binding of the gfx950 shifted-window attention library (libswin_wmsa.so).
+
+Argument marshalling only: every step of the forward runs in the HIP kernels
+behind the C ABI declared in include/swin_wmsa.h.  torch supplies device memory
+and the current stream.  There is no CPU path: the functions raise if the
+library is missing or a tensor is not on the GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libswin_wmsa.so")
+
+SWIN_OK = 0
+SWIN_V1, SWIN_V2 = 1, 2
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_EXPORTS = ("swin_status_str", "swin_abi_version", "swin_partition_shift", "swin_reverse_unshift",
+            "swin_cpb_table", "swin_wmsa_workspace_size", "swin_wmsa_fwd")
+
+
+class SwinDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("W", ctypes.c_int),
+                ("C", ctypes.c_int), ("heads", ctypes.c_int), ("M", ctypes.c_int),
+                ("s", ctypes.c_int), ("mode", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("scale", ctypes.c_float), ("tau_min", ctypes.c_float)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library and declare the C signatures (no GPU work)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m shifted_window_attention_roll_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int
+    lib.swin_status_str.restype = ctypes.c_char_p
+    lib.swin_status_str.argtypes = [st]
+    lib.swin_abi_version.restype = i
+    lib.swin_abi_version.argtypes = []
+    for name in ("swin_partition_shift", "swin_reverse_unshift"):
+        fn = getattr(lib, name)
+        fn.restype = st
+        fn.argtypes = [vp, vp, i, i, i, i, i, i, i, vp]
+    lib.swin_cpb_table.restype = st
+    lib.swin_cpb_table.argtypes = [vp, vp, vp, vp, i, i, i, f, vp, vp]
+    lib.swin_wmsa_workspace_size.restype = ctypes.c_size_t
+    lib.swin_wmsa_workspace_size.argtypes = [ctypes.POINTER(SwinDesc)]
+    lib.swin_wmsa_fwd.restype = st
+    lib.swin_wmsa_fwd.argtypes = [ctypes.POINTER(SwinDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  ctypes.c_size_t, vp]
+    _lib = lib
+    return lib
+
+
+class SwinError(RuntimeError):
+    def __init__(self, code: int):
+        self.code = code
+        super().__init__(load_library().swin_status_str(code).decode())
+
+
+def _check(code: int) -> None:
+    if code != SWIN_OK:
+        raise SwinError(code)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU (no CPU path exists)")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(B, H, W, C, heads, M, s, mode="v1", dtype=torch.bfloat16, scale=0.0,
+              tau_min=0.0) -> SwinDesc:
+    m = {"v1": SWIN_V1, "v2": SWIN_V2}[mode] if isinstance(mode, str) else int(mode)
+    dt = _DT[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return SwinDesc(B, H, W, C, heads, M, s, m, dt, float(scale), float(tau_min))
+
+
+def workspace_size(desc: SwinDesc) -> int:
+    return int(load_library().swin_wmsa_workspace_size(ctypes.byref(desc)))
+
+
+def partition_shift(x: torch.Tensor, M: int, s: int, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """x [B, H, W, C] -> [B*nW, M*M, C] (bit-exact permutation)."""
+    B, H, W, C = x.shape
+    if out is None:
+        out = torch.empty(((B * H * W) // (M * M) if M else 0, M * M, C), dtype=x.dtype,
+                          device=x.device)
+    _check(load_library().swin_partition_shift(_ptr(x), _ptr(out), B, H, W, C, M, s,
+                                               _DT[x.dtype], _stream(stream)))
+    return out
+
+
+def reverse_unshift(xw: torch.Tensor, B: int, H: int, W: int, M: int, s: int,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """xw [B*nW, M*M, C] -> [B, H, W, C] (inverse of partition_shift)."""
+    C = xw.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, W, C), dtype=xw.dtype, device=xw.device)
+    _check(load_library().swin_reverse_unshift(_ptr(xw), _ptr(out), B, H, W, C, M, s,
+                                               _DT[xw.dtype], _stream(stream)))
+    return out
+
+
+def cpb_table(w1, b1, w2, b2, M: int, coord_scale: float = 0.0,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """V2 continuous position bias table [(2M-1)^2, heads], float32."""
+    hidden, heads = w1.shape[0], w2.shape[0]
+    if out is None:
+        out = torch.empty(((2 * M - 1) ** 2, heads), dtype=torch.float32, device=w1.device)
+    _check(load_library().swin_cpb_table(_ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), hidden, heads,
+                                         M, float(coord_scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def wmsa_fwd(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv: Optional[torch.Tensor],
+             w_proj: torch.Tensor, b_proj: Optional[torch.Tensor], bias_table: torch.Tensor,
+             M: int, s: int, heads: int, mode: str = "v1", tau: Optional[torch.Tensor] = None,
+             scale: float = 0.0, tau_min: float = 0.0, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Shifted-window MHSA block forward; y has the shape and dtype of x."""
+    B, H, W, C = x.shape
+    desc = make_desc(B, H, W, C, heads, M, s, mode, x.dtype, scale, tau_min)
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(desc), 1), dtype=torch.uint8, device=x.device)
+    _check(load_library().swin_wmsa_fwd(
+        ctypes.byref(desc), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj), _ptr(b_proj),
+        _ptr(bias_table), _ptr(tau), _ptr(out), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return out
+
+
+__all__ = ["load_library", "make_desc", "workspace_size", "partition_shift", "reverse_unshift",
+           "cpb_table", "wmsa_fwd", "SwinDesc", "SwinError", "LIB_PATH"]

@@ -1,0 +1,207 @@
+// C ABI: argument validation, workspace layout and kernel dispatch.
+// Declarations and the contract of every entry point are in include/swin_wmsa.h.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/swin_wmsa.h"
+#include "launch.hpp"
+
+using namespace swin;
+
+namespace {
+
+constexpr int kHeadDim = 32;
+
+int elem_bytes(int dt) { return dt == SWIN_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+swin_status check_geometry(int B, int H, int W, int C, int M, int s) {
+  if (B < 0 || H < 1 || W < 1 || C < 1 || M < 1) return SWIN_ERR_SHAPE;
+  if (H % M || W % M) return SWIN_ERR_SHAPE;
+  if (s < 0 || s >= M) return SWIN_ERR_SHAPE;
+  if ((int64_t)B * H * W > INT32_MAX) return SWIN_ERR_UNSUPPORTED;
+  return SWIN_OK;
+}
+
+Geom make_geom(int B, int H, int W, int C, int M, int s, int heads) {
+  Geom g;
+  g.B = B; g.H = H; g.W = W; g.C = C; g.M = M; g.s = s;
+  g.nWx = W / M;
+  g.nW = (H / M) * (W / M);
+  g.N = M * M;
+  g.heads = heads;
+  return g;
+}
+
+swin_status from_hip(hipError_t e) { return e == hipSuccess ? SWIN_OK : SWIN_ERR_HIP; }
+
+// Storage type of q and k: V2 with 16-bit I/O keeps the normalised, 1/tau-scaled
+// q and k in float16 (|q| <= log2(e)/0.01, |k| <= 1), whose 11-bit significand
+// keeps the cosine logits accurate when 1/tau reaches 100.
+int qk_type(const swin_wmsa_desc* d) {
+  if (d->dtype == SWIN_F32) return kF32;
+  if (d->mode == SWIN_V2) return kF16;
+  return d->dtype == SWIN_F16 ? kF16 : kBF16;
+}
+
+struct WsLayout {
+  size_t q, k, v, o, total;
+};
+
+WsLayout ws_layout(const swin_wmsa_desc* d) {
+  const size_t tokens = (size_t)d->B * d->H * d->W;
+  const size_t e = elem_bytes(d->dtype);
+  const size_t eq = qk_type(d) == kF32 ? 4 : 2;
+  WsLayout L;
+  L.q = 0;
+  L.k = round_up(L.q + tokens * d->C * eq, 256);
+  L.v = round_up(L.k + tokens * d->C * eq, 256);
+  L.o = round_up(L.v + tokens * d->C * e, 256);
+  L.total = round_up(L.o + tokens * d->C * e, 256);
+  return L;
+}
+
+swin_status validate_desc(const swin_wmsa_desc* d) {
+  if (!d) return SWIN_ERR_NULL;
+  if (d->mode != SWIN_V1 && d->mode != SWIN_V2) return SWIN_ERR_DTYPE;
+  if (d->dtype != SWIN_F32 && d->dtype != SWIN_F16 && d->dtype != SWIN_BF16) return SWIN_ERR_DTYPE;
+  swin_status st = check_geometry(d->B, d->H, d->W, d->C, d->M, d->s);
+  if (st != SWIN_OK) return st;
+  if (d->heads < 1 || d->C % d->heads) return SWIN_ERR_SHAPE;
+  if (d->C / d->heads != kHeadDim) return SWIN_ERR_UNSUPPORTED;
+  if (d->M > max_window(elem_bytes(d->dtype))) return SWIN_ERR_UNSUPPORTED;
+  return SWIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* swin_status_str(swin_status s) {
+  switch (s) {
+    case SWIN_OK: return "SWIN_OK";
+    case SWIN_ERR_NULL: return "SWIN_ERR_NULL: a required pointer is NULL";
+    case SWIN_ERR_SHAPE: return "SWIN_ERR_SHAPE: inconsistent sizes (H % M, W % M, shift range, C % heads)";
+    case SWIN_ERR_DTYPE: return "SWIN_ERR_DTYPE: unknown dtype or mode";
+    case SWIN_ERR_UNSUPPORTED: return "SWIN_ERR_UNSUPPORTED: head dim must be 32, window side within the kernel limit";
+    case SWIN_ERR_ALIAS: return "SWIN_ERR_ALIAS: an output overlaps an input or the workspace";
+    case SWIN_ERR_WORKSPACE: return "SWIN_ERR_WORKSPACE: workspace too small";
+    case SWIN_ERR_ALIGN: return "SWIN_ERR_ALIGN: pointer not 16-byte aligned";
+    case SWIN_ERR_HIP: return "SWIN_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown swin_status";
+}
+
+int swin_abi_version(void) { return SWIN_WMSA_ABI_VERSION; }
+
+static swin_status index_map_common(const void* in, void* out, int B, int H, int W, int C, int M,
+                                    int s, swin_dtype dt, void* stream, bool reverse) {
+  if (dt != SWIN_F32 && dt != SWIN_F16 && dt != SWIN_BF16) return SWIN_ERR_DTYPE;
+  swin_status st = check_geometry(B, H, W, C, M, s);
+  if (st != SWIN_OK) return st;
+  if (B == 0) return SWIN_OK;
+  if (!in || !out) return SWIN_ERR_NULL;
+  const size_t bytes = (size_t)B * H * W * C * elem_bytes(dt);
+  if (overlap(in, bytes, out, bytes)) return SWIN_ERR_ALIAS;
+  if (!aligned16(in) || !aligned16(out)) return SWIN_ERR_ALIGN;
+  Geom g = make_geom(B, H, W, C, M, s, 1);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = reverse ? launch_reverse_unshift(in, out, g, elem_bytes(dt), hs)
+                         : launch_partition_shift(in, out, g, elem_bytes(dt), hs);
+  return from_hip(e);
+}
+
+swin_status swin_partition_shift(const void* x, void* xw, int B, int H, int W, int C, int M, int s,
+                                 swin_dtype dt, void* stream) {
+  return index_map_common(x, xw, B, H, W, C, M, s, dt, stream, false);
+}
+
+swin_status swin_reverse_unshift(const void* xw, void* x, int B, int H, int W, int C, int M,
+                                 int s, swin_dtype dt, void* stream) {
+  return index_map_common(xw, x, B, H, W, C, M, s, dt, stream, true);
+}
+
+swin_status swin_cpb_table(const float* w1, const float* b1, const float* w2, const float* b2,
+                           int hidden, int heads, int M, float coord_scale, float* table,
+                           void* stream) {
+  if (!w1 || !b1 || !w2 || !table) return SWIN_ERR_NULL;
+  if (hidden < 1 || hidden > 4096 || heads < 1 || heads > 64 || M < 1 || M > 32)
+    return SWIN_ERR_SHAPE;
+  const size_t tbytes = (size_t)(2 * M - 1) * (2 * M - 1) * heads * sizeof(float);
+  if (overlap(table, tbytes, w1, (size_t)hidden * 2 * 4) || overlap(table, tbytes, b1, hidden * 4u) ||
+      overlap(table, tbytes, w2, (size_t)heads * hidden * 4) ||
+      (b2 && overlap(table, tbytes, b2, heads * 4u)))
+    return SWIN_ERR_ALIAS;
+  if (!(coord_scale > 0.0f)) coord_scale = M > 1 ? 8.0f / (float)(M - 1) : 1.0f;
+  return from_hip(launch_cpb_table(w1, b1, w2, b2, hidden, heads, M, coord_scale, table,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
+  if (validate_desc(d) != SWIN_OK || d->B == 0) return 0;
+  return ws_layout(d).total;
+}
+
+swin_status swin_wmsa_fwd(const swin_wmsa_desc* d, const void* x, const void* w_qkv,
+                          const void* b_qkv, const void* w_proj, const void* b_proj,
+                          const float* bias_table, const float* tau, void* y, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  swin_status st = validate_desc(d);
+  if (st != SWIN_OK) return st;
+  if (d->B == 0) return SWIN_OK;
+  if (!x || !w_qkv || !w_proj || !bias_table || !y || !workspace) return SWIN_ERR_NULL;
+  if (d->mode == SWIN_V2 && !tau) return SWIN_ERR_NULL;
+  const WsLayout L = ws_layout(d);
+  if (ws_bytes < L.total) return SWIN_ERR_WORKSPACE;
+  const size_t e = elem_bytes(d->dtype);
+  const size_t act = (size_t)d->B * d->H * d->W * d->C * e;
+  const size_t C = d->C;
+  if (overlap(y, act, x, act) || overlap(y, act, workspace, L.total) ||
+      overlap(workspace, L.total, x, act) || overlap(y, act, w_qkv, 3 * C * C * e) ||
+      overlap(y, act, w_proj, C * C * e) || overlap(workspace, L.total, w_qkv, 3 * C * C * e) ||
+      overlap(workspace, L.total, w_proj, C * C * e))
+    return SWIN_ERR_ALIAS;
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(w_proj) || !aligned16(y) ||
+      !aligned16(workspace))
+    return SWIN_ERR_ALIGN;
+
+  FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.g = make_geom(d->B, d->H, d->W, d->C, d->M, d->s, d->heads);
+  p.io = d->dtype == SWIN_F32 ? kF32 : d->dtype == SWIN_F16 ? kF16 : kBF16;
+  p.qk = qk_type(d);
+  p.v2 = d->mode == SWIN_V2;
+  const float scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)kHeadDim);
+  p.q_mult = scale * kLog2e;
+  p.tau_min = d->tau_min > 0.0f ? d->tau_min : 0.01f;
+  p.eps = 1e-12f;
+  p.x = x;
+  p.w_qkv = w_qkv;
+  p.b_qkv = b_qkv;
+  p.w_proj = w_proj;
+  p.b_proj = b_proj;
+  p.table = bias_table;
+  p.tau = tau;
+  p.y = y;
+  char* ws = static_cast<char*>(workspace);
+  p.buf.q = ws + L.q;
+  p.buf.k = ws + L.k;
+  p.buf.v = ws + L.v;
+  p.buf.o = ws + L.o;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t err = launch_qkv_gemm(p, hs);
+  if (err == hipSuccess) err = launch_window_attn(p, hs);
+  if (err == hipSuccess) err = launch_proj_gemm(p, hs);
+  return from_hip(err);
+}
+
+}  // extern "C"

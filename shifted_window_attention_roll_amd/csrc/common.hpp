@@ -1,0 +1,96 @@
+// Shared device helpers for the gfx950 shifted-window attention kernels:
+// element types, 16-byte fragment loads, the 16x16x32 matrix-core step and the
+// window geometry (cyclic shift + window partition as pure index arithmetic).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swin {
+
+typedef _Float16 h16;
+typedef __bf16 b16;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+using vec8 = T __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Eight consecutive elements (one lane's K-slice of a 16x16x32 operand).
+template <typename T>
+__device__ __forceinline__ vec8<T> load8(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    return __builtin_bit_cast(vec8<T>, u);
+  } else {
+    uint4 u0 = reinterpret_cast<const uint4*>(p)[0];
+    uint4 u1 = reinterpret_cast<const uint4*>(p)[1];
+    struct P { uint4 a, b; } pr{u0, u1};
+    return __builtin_bit_cast(vec8<T>, pr);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const vec8<T>& v) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint4*>(p) = __builtin_bit_cast(uint4, v);
+  } else {
+    struct P { uint4 a, b; };
+    P pr = __builtin_bit_cast(P, v);
+    reinterpret_cast<uint4*>(p)[0] = pr.a;
+    reinterpret_cast<uint4*>(p)[1] = pr.b;
+  }
+}
+
+// acc += A(16x32) * B(32x16) on the matrix cores.  Lane l supplies row / column
+// (l % 16) and the K-slice 8*(l/16) .. 8*(l/16)+7 of each operand; the result
+// tile holds, in lane l, column (l % 16) of rows 4*(l/16) .. 4*(l/16)+3.
+// For float32 the slice is fed as eight 16x16x4 steps; A and B pair their K
+// indices identically, so the sum covers the same 32 products.
+__device__ __forceinline__ f32x4 mma_16x16x32(const vec8<h16>& a, const vec8<h16>& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_16x16x32(const vec8<b16>& a, const vec8<b16>& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_16x16x32(const vec8<float>& a, const vec8<float>& b, f32x4 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v) { return (T)v; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Window geometry.  Window w = b*nW + wy*nWx + wx, token t = ty*M + tx; the
+// slot holds shifted-frame (wy*M+ty, wx*M+tx), i.e. original position
+// ((wy*M+ty+s) mod H, (wx*M+tx+s) mod W).
+struct Geom {
+  int B, H, W, C, M, s, nWx, nW, N, heads;
+};
+
+__device__ __forceinline__ int64_t src_token(const Geom& g, int r) {
+  int w = r / g.N;
+  int t = r - w * g.N;
+  int b = w / g.nW;
+  int wl = w - b * g.nW;
+  int wy = wl / g.nWx;
+  int wx = wl - wy * g.nWx;
+  int ty = t / g.M;
+  int tx = t - ty * g.M;
+  int y = wy * g.M + ty + g.s;
+  if (y >= g.H) y -= g.H;
+  int x = wx * g.M + tx + g.s;
+  if (x >= g.W) x -= g.W;
+  return ((int64_t)b * g.H + y) * g.W + x;
+}
+
+// Slice of a shifted-frame coordinate v on an axis of length L (region mask).
+__device__ __forceinline__ int axis_slice(int v, int L, int M, int s) {
+  return v < L - M ? 0 : (v < L - s ? 1 : 2);
+}
+
+}  // namespace swin

@@ -1,0 +1,56 @@
+// Host-side launchers of the device kernels (one definition per .hip file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.hpp"
+
+namespace swin {
+
+// Element type of x / y / weights: 0 = float32, 1 = float16, 2 = bfloat16.
+enum IoType { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Per-window intermediates written by the QKV projection and read by the
+// window attention.  Layout of q, k, v: [B*nW, heads, N, 32] (one window-head
+// block contiguous, token-major, head dim fastest); o: [B*nW*N, C] window order.
+struct QkvBuffers {
+  void* q;  // qk_type
+  void* k;  // qk_type
+  void* v;  // io type
+  void* o;  // io type
+};
+
+struct FwdParams {
+  Geom g;
+  int io;          // IoType of x, y, weights, linear biases
+  int qk;          // IoType of the stored q and k
+  bool v2;         // scaled cosine attention
+  float q_mult;    // V1: scale * log2(e) folded into q
+  float tau_min;   // V2 clip
+  float eps;       // V2 norm clamp
+  const void* x;
+  const void* w_qkv;
+  const void* b_qkv;   // may be null
+  const void* w_proj;
+  const void* b_proj;  // may be null
+  const float* table;  // [(2M-1)^2, heads]
+  const float* tau;    // [heads] (V2)
+  void* y;
+  QkvBuffers buf;
+};
+
+hipError_t launch_partition_shift(const void* x, void* xw, const Geom& g, int elem_bytes,
+                                  hipStream_t st);
+hipError_t launch_reverse_unshift(const void* xw, void* x, const Geom& g, int elem_bytes,
+                                  hipStream_t st);
+hipError_t launch_cpb_table(const float* w1, const float* b1, const float* w2, const float* b2,
+                            int hidden, int heads, int M, float coord_scale, float* table,
+                            hipStream_t st);
+hipError_t launch_qkv_gemm(const FwdParams& p, hipStream_t st);
+hipError_t launch_window_attn(const FwdParams& p, hipStream_t st);
+hipError_t launch_proj_gemm(const FwdParams& p, hipStream_t st);
+
+// Largest window side the attention kernel stages in LDS for an element size.
+inline int max_window(int io_bytes) { return io_bytes == 4 ? 16 : 24; }
+
+}  // namespace swin

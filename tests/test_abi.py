@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every symbol the header declares, and rejects
+invalid calls on the host before launching anything.  CPU only: no call here
+reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import shifted_window_attention_roll_amd as swin
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swin_wmsa.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, WS, ALIGN = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(swin.LIB_PATH):
+        from shifted_window_attention_roll_amd import build
+        build.build()
+    return swin.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swin_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) == set(swin._EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.swin_abi_version() == 1
+    for code in range(9):
+        s = lib.swin_status_str(code).decode()
+        assert s.startswith("SWIN_")
+    assert lib.swin_status_str(99).decode() == "unknown swin_status"
+
+
+def _desc(**kw):
+    base = dict(B=2, H=56, W=56, C=96, heads=3, M=7, s=3, mode="v1", dtype=torch.float16)
+    base.update(kw)
+    return swin.make_desc(**base)
+
+
+def test_workspace_size(lib):
+    d = _desc()
+    T = 2 * 56 * 56
+    assert swin.workspace_size(d) >= 4 * T * 96 * 2
+    assert swin.workspace_size(_desc(B=0)) == 0
+    assert swin.workspace_size(_desc(H=50)) == 0          # invalid -> 0
+    # V2 with bf16 keeps q and k in float16: same byte count as bf16
+    assert swin.workspace_size(_desc(mode="v2", dtype=torch.bfloat16)) == swin.workspace_size(d)
+    assert swin.workspace_size(_desc(dtype=torch.float32)) >= 4 * T * 96 * 4
+
+
+FAKE = 1 << 20  # host-side stand-in addresses; validation fails before any use
+
+
+def _fwd(lib, d, x=FAKE, wq=FAKE * 2, wp=FAKE * 3, tab=FAKE * 4, tau=FAKE * 5, y=FAKE * 8,
+         ws=FAKE * 16, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.swin_wmsa_workspace_size(ctypes.byref(d))
+    return lib.swin_wmsa_fwd(ctypes.byref(d), x, wq, None, wp, None, tab, tau, y, ws, ws_bytes, None)
+
+
+def test_fwd_rejects_before_launch(lib):
+    small = _desc(B=1, H=7, W=7, C=32, heads=1, M=7, s=3)
+    assert _fwd(lib, _desc(H=50)) == SHAPE                   # H % M
+    assert _fwd(lib, _desc(s=7)) == SHAPE                    # s >= M
+    assert _fwd(lib, _desc(s=-1)) == SHAPE
+    assert _fwd(lib, _desc(heads=5)) == SHAPE                # C % heads
+    assert _fwd(lib, _desc(heads=1)) == UNSUP                # head dim 96
+    assert _fwd(lib, _desc(M=28, s=0)) == UNSUP              # window beyond the LDS limit
+    assert _fwd(lib, _desc(M=28, s=0, H=56)) == UNSUP
+    assert _fwd(lib, _desc(mode=7)) == DTYPE
+    assert _fwd(lib, _desc(dtype=9)) == DTYPE
+    assert _fwd(lib, _desc(B=0)) == OK                        # empty: nothing to do
+    assert _fwd(lib, small, x=None) == NULL
+    assert _fwd(lib, small, tab=None) == NULL
+    assert _fwd(lib, _desc(B=1, H=7, W=7, C=32, heads=1, M=7, s=3, mode="v2"), tau=None) == NULL
+    assert _fwd(lib, small, ws_bytes=16) == WS
+    assert _fwd(lib, small, y=FAKE + 64) == ALIAS             # y overlaps x
+    assert _fwd(lib, small, ws=FAKE * 8 + 128) == ALIAS       # workspace overlaps y
+    assert _fwd(lib, small, x=FAKE + 8) == ALIGN
+    assert lib.swin_wmsa_fwd(None, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, 0, None) == NULL
+
+
+def test_index_maps_reject_before_launch(lib):
+    f = lib.swin_partition_shift
+    assert f(FAKE, FAKE * 4, 1, 14, 14, 8, 4, 1, 1, None) == SHAPE
+    assert f(FAKE, FAKE * 4, 1, 14, 14, 8, 7, 7, 1, None) == SHAPE
+    assert f(FAKE, FAKE * 4, 1, 14, 14, 8, 7, 3, 5, None) == DTYPE
+    assert f(None, FAKE * 4, 1, 14, 14, 8, 7, 3, 1, None) == NULL
+    assert f(FAKE, FAKE + 16, 1, 14, 14, 8, 7, 3, 1, None) == ALIAS
+    assert f(FAKE + 2, FAKE * 4, 1, 14, 14, 8, 7, 3, 1, None) == ALIGN
+    assert f(FAKE, FAKE * 4, 0, 14, 14, 8, 7, 3, 1, None) == OK
+    assert lib.swin_reverse_unshift(FAKE, FAKE * 4, 1, 14, 12, 8, 7, 3, 1, None) == SHAPE
+
+
+def test_cpb_rejects_before_launch(lib):
+    f = lib.swin_cpb_table
+    assert f(None, FAKE, FAKE, None, 512, 4, 16, 0.0, FAKE * 8, None) == NULL
+    assert f(FAKE, FAKE * 2, FAKE * 3, None, 0, 4, 16, 0.0, FAKE * 8, None) == SHAPE
+    assert f(FAKE, FAKE * 2, FAKE * 3, None, 512, 4, 33, 0.0, FAKE * 8, None) == SHAPE
+    assert f(FAKE, FAKE * 2, FAKE * 3, None, 512, 4, 16, 0.0, FAKE + 64, None) == ALIAS
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    x = torch.zeros(1, 7, 7, 32)
+    with pytest.raises(ValueError):
+        swin.partition_shift(x, 7, 3)

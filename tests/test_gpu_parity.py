@@ -1,0 +1,173 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on seeded
+inputs.  Index maps bit-exact; CPB table within 1e-5; the block forward within
+max-abs 1e-4 (float32) or max-abs 2e-2 and relative L2 5e-3 (fp16 / bf16)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import swin_oracle as so
+
+import helpers
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import shifted_window_attention_roll_amd as swin
+    swin.load_library()
+    return swin
+
+
+# --- index maps: bit-exact on random bit patterns ------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("B,H,W,C,M,s", [
+    (2, 14, 14, 96, 7, 3), (1, 56, 56, 96, 7, 0), (3, 12, 20, 40, 4, 1), (1, 16, 16, 8, 16, 8),
+    (1, 24, 48, 128, 24, 12), (2, 6, 6, 3, 3, 2), (1, 5, 5, 1, 5, 4)])
+def test_index_maps_bit_exact(gpu, dtype, B, H, W, C, M, s):
+    _say(f"index_map dtype={dtype} B={B} H={H} W={W} C={C} M={M} s={s}")
+    x = workloads.random_bits((B, H, W, C), dtype, seed=B * 1000 + H + C + s)
+    xi = x.view(torch.int32 if dtype == "fp32" else torch.int16)
+    ref = so.partition_shift(xi.numpy(), M, s)
+    xw = gpu.partition_shift(x.cuda(), M, s)
+    got = xw.cpu().view(xi.dtype).numpy()
+    assert np.array_equal(got, ref)
+    back = gpu.reverse_unshift(xw, B, H, W, M, s)
+    assert np.array_equal(back.cpu().view(xi.dtype).numpy(), xi.numpy())
+
+
+def test_index_map_max_size(gpu):
+    """SwinV2-G-like 384x384x512 bf16 map, every element, bit-exact."""
+    _say("index_map 384x384x512 bf16")
+    x = workloads.random_bits((1, 384, 384, 512), "bf16", seed=77)
+    xi = x.view(torch.int16).numpy()
+    got = gpu.partition_shift(x.cuda(), 24, 12).cpu().view(torch.int16).numpy()
+    assert np.array_equal(got, so.partition_shift(xi, 24, 12))
+
+
+# --- CPB table -----------------------------------------------------------------
+
+@pytest.mark.parametrize("M,heads,hidden", [(16, 4, 512), (24, 16, 512), (7, 3, 64), (2, 1, 8)])
+def test_cpb_table(gpu, M, heads, hidden):
+    _say(f"cpb M={M} heads={heads} hidden={hidden}")
+    case = workloads.make_case(1, M, M, 32 * heads, heads, M, (0,), "bf16", "v2", seed=M + heads,
+                               cpb_hidden=hidden)
+    blk = case.blocks[0]
+    blk.cpb_b2 = torch.randn(heads, generator=torch.Generator().manual_seed(3))
+    got = helpers.gpu_table(case, blk).cpu().double().numpy()
+    ref = helpers.oracle_table(case, blk)
+    assert np.max(np.abs(got - ref)) <= 1e-5
+    # second bias absent (NULL) and raw coordinates
+    got2 = gpu.cpb_table(blk.cpb_w1.cuda(), blk.cpb_b1.cuda(), blk.cpb_w2.cuda(), None, M,
+                         coord_scale=1.0).cpu().double().numpy()
+    ref2 = so.cpb_table(workloads.f64(blk.cpb_w1), workloads.f64(blk.cpb_b1),
+                        workloads.f64(blk.cpb_w2), None, M, coord_scale=1.0)
+    assert np.max(np.abs(got2 - ref2)) <= 1e-5
+
+
+# --- block forward, small cases spanning several tiles and a ragged tail --------
+
+SMALL = [
+    # B, H, W, C, heads, M, s, dtype, mode, bias_std
+    (2, 28, 28, 96, 3, 7, 3, "fp32", "v1", 0.1),
+    (2, 28, 28, 96, 3, 7, 3, "fp16", "v1", 0.1),
+    (2, 28, 28, 96, 3, 7, 0, "bf16", "v1", 0.0),
+    (3, 14, 21, 64, 2, 7, 3, "bf16", "v1", 0.1),     # C = 64 projection tiles, ragged rows
+    (2, 14, 14, 160, 5, 7, 3, "fp16", "v1", 0.1),    # C = 160: 32-wide projection tiles
+    (1, 16, 16, 32, 1, 16, 8, "fp32", "v2", 0.1),    # one head, window = image, shifted
+    (2, 32, 32, 128, 4, 16, 8, "bf16", "v2", 0.1),
+    (2, 32, 32, 128, 4, 16, 8, "fp16", "v2", 0.0),
+    (1, 48, 48, 64, 2, 24, 12, "bf16", "v2", 0.1),
+    (1, 24, 24, 64, 2, 24, 12, "fp16", "v1", 0.1),   # window = image, shifted, N = 576
+    (2, 8, 8, 96, 3, 8, 4, "fp32", "v1", 0.1),
+    (1, 12, 12, 32, 1, 6, 5, "bf16", "v2", 0.1),
+    (1, 10, 10, 32, 1, 5, 2, "fp32", "v2", 0.1),     # N = 25: a single padded key block
+]
+
+
+@pytest.mark.parametrize("B,H,W,C,heads,M,s,dtype,mode,bias_std", SMALL)
+def test_wmsa_small(gpu, B, H, W, C, heads, M, s, dtype, mode, bias_std):
+    _say(f"wmsa small B={B} H={H} W={W} C={C} heads={heads} M={M} s={s} {dtype} {mode}")
+    case = workloads.make_case(B, H, W, C, heads, M, (s,), dtype, mode, seed=H * 100 + C + s,
+                               w_std=0.08, bias_std=bias_std, tau="uniform")
+    blk = case.blocks[0]
+    x = case.x.cuda()
+    y = helpers.run_gpu_block(case, blk, x)
+    torch.cuda.synchronize()
+    ref = helpers.run_oracle_block(case, blk, workloads.f64(case.x))
+    helpers.assert_close(workloads.f64(y.cpu()), ref, dtype, "small")
+
+
+def test_wmsa_empty_batch(gpu):
+    case = workloads.make_case(1, 14, 14, 96, 3, 7, (3,), "bf16", "v1", seed=1)
+    blk = case.blocks[0]
+    x = torch.empty((0, 14, 14, 96), dtype=torch.bfloat16, device="cuda")
+    y = helpers.run_gpu_block(case, blk, x)
+    assert y.shape == x.shape
+
+
+def test_wmsa_deterministic_and_every_output_written(gpu):
+    _say("determinism")
+    case = workloads.make_case(4, 32, 32, 128, 4, 16, (8,), "bf16", "v2", seed=5, tau="uniform")
+    blk = case.blocks[0]
+    x = case.x.cuda()
+    out = torch.full_like(x, float("nan"))
+    y1 = helpers.run_gpu_block(case, blk, x, out=out).clone()
+    out.fill_(float("nan"))
+    y2 = helpers.run_gpu_block(case, blk, x, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1.float()).all()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+# --- the five workloads at full size --------------------------------------------
+
+def _workload_parity(gpu, name, n_random, full=False):
+    case = workloads.make_workload(name)
+    x = case.x.cuda()
+    x_host = case.x
+    for bi, blk in enumerate(case.blocks):
+        _say(f"workload {name} block {bi} s={blk.s}")
+        y = helpers.run_gpu_block(case, blk, x)
+        y_host = y.cpu()
+        x64 = workloads.f64(x_host)
+        if full:
+            ref = helpers.run_oracle_block(case, blk, x64)
+            got = workloads.f64(y_host)
+        else:
+            wins = helpers.sample_windows(case.B, case.H, case.W, case.M, n_random, seed=bi + 11)
+            tok, ref = helpers.run_oracle_block(case, blk, x64, windows=wins)
+            got = workloads.f64(y_host).reshape(-1, case.C)[tok]
+        helpers.assert_close(got, ref, case.dtype, f"{name} block {bi}")
+        x, x_host = y, y_host  # the next block consumes this block's output
+
+
+def test_workload_swin_t_stage1_b1_fp32_full(gpu):
+    _workload_parity(gpu, "swin_t_stage1_b1_fp32", 0, full=True)
+
+
+def test_workload_swin_t_stage1_b64_fp16(gpu):
+    _workload_parity(gpu, "swin_t_stage1_b64_fp16", 24)
+
+
+def test_workload_swin_b_stage3_b64_bf16(gpu):
+    _workload_parity(gpu, "swin_b_stage3_b64_bf16", 24)
+
+
+def test_workload_swinv2_b_stage1_w16_bf16(gpu):
+    _workload_parity(gpu, "swinv2_b_stage1_w16_bf16", 16)
+
+
+def test_workload_swinv2_g_stage1_384_w24_bf16(gpu):
+    _workload_parity(gpu, "swinv2_g_stage1_384_w24_bf16", 12)
