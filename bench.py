@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Throughput of the shifted-window attention block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one pass of the whole forward over one batch: for the default
+workload (Swin-T stage 1, batch 64, 56x56 tokens, C = 96, 3 heads, window 7,
+fp16) that is a W-MSA block (shift 0) followed by an SW-MSA block (shift 3).
+Inputs are seeded synthetic tensors already resident in HBM; x is rotated over
+enough copies to exceed the 256 MB last-level cache.
+
+Prints ONE JSON line on stdout (logs go to stderr) with:
+  value        tokens/s over the timed steps (block-tokens: every token of every
+               block forward counts once),
+  roofline     the dominant kernel's achieved algorithmic bytes or flops per
+               launch divided by its average launch duration, measured with HIP
+               events recorded by the library around each of its kernels on the
+               stream they run on,
+  cpu_baseline the float64 CPU oracle timed on a bounded sample of the same
+               workload on this host,
+  workloads    the same measurement for the other workload shapes.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import glob
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "shifted-window attention tokens/s + TFLOP/s as % of MFMA peak, 1 MI355X"
+MAIN = "swin_t_stage1_b64_fp16"
+PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0, "fp32": 157.3}   # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0                                             # HBM3E, MI355X
+ELEM = {"fp32": 4, "fp16": 2, "bf16": 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops_per_token(C, N):
+    """Algorithmic flops per token: QKV 6C^2, QK^T 2NC, AV 2NC, projection 2C^2."""
+    return 8 * C * C + 4 * N * C
+
+
+def stage_work(case):
+    """Algorithmic (flops, bytes) per launch of each kernel of the three-kernel
+    forward: the data its interface must move once (activations in and out, the
+    weights and the bias table), not what it re-reads."""
+    T, C, N, heads = case.tokens, case.C, case.M * case.M, case.heads
+    e = ELEM[case.dtype]
+    eqk = 2 if (case.mode == "v2" and case.dtype != "fp32") else e
+    tab = (2 * case.M - 1) ** 2 * heads * 4
+    return {
+        "qkv_gemm_kernel": (6 * C * C * T, T * (C * e + 2 * C * eqk + C * e) + 3 * C * C * e),
+        "window_attn_kernel": (4 * N * C * T, T * (2 * C * eqk + C * e + C * e) + tab),
+        "proj_gemm_kernel": (2 * C * C * T, T * 2 * C * e + C * C * e),
+    }
+
+
+class HipEvents:
+    """Raw hipEvent_t handles for the library's per-kernel event records."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(h.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+class Runner:
+    """Device-resident inputs of one workload and one forward step."""
+
+    def __init__(self, name, min_rotate_bytes=512 << 20, max_copies=16):
+        import torch
+        import shifted_window_attention_roll_amd as swin
+        import workloads
+        self.swin, self.torch = swin, torch
+        self.name = name
+        self.case = case = workloads.make_workload(name)
+        dev = "cuda"
+        xb = case.x.numel() * case.x.element_size()
+        self.copies = max(1, min(max_copies, math.ceil(min_rotate_bytes / max(xb, 1))))
+        x0 = case.x.to(dev)
+        self.xs = [x0] + [x0.clone() for _ in range(self.copies - 1)]
+        self.blocks = []
+        for blk in case.blocks:
+            if case.mode == "v1":
+                table = blk.table.to(dev)
+            else:
+                table = swin.cpb_table(blk.cpb_w1.to(dev), blk.cpb_b1.to(dev), blk.cpb_w2.to(dev),
+                                       blk.cpb_b2.to(dev), case.M)
+            self.blocks.append(dict(
+                s=blk.s, w_qkv=blk.w_qkv.to(dev), b_qkv=blk.b_qkv.to(dev),
+                w_proj=blk.w_proj.to(dev), b_proj=blk.b_proj.to(dev), table=table,
+                tau=None if blk.tau is None else blk.tau.to(dev),
+                out=torch.empty_like(x0)))
+        desc = swin.make_desc(case.B, case.H, case.W, case.C, case.heads, case.M,
+                              case.blocks[0].s, case.mode, case.torch_dtype)
+        self.ws = torch.empty(swin.workspace_size(desc), dtype=torch.uint8, device=dev)
+        self.kernels = swin.kernel_names(desc)
+        self.tokens_per_step = case.tokens * len(case.blocks)
+        self.flops_per_step = flops_per_token(case.C, case.M * case.M) * self.tokens_per_step
+
+    def step(self, i, events=None):
+        x = self.xs[i % self.copies]
+        for bi, b in enumerate(self.blocks):
+            ev = None if events is None else events[bi]
+            x = self.swin.wmsa_fwd(x, b["w_qkv"], b["b_qkv"], b["w_proj"], b["b_proj"], b["table"],
+                                   self.case.M, b["s"], self.case.heads, self.case.mode,
+                                   tau=b["tau"], out=b["out"], workspace=self.ws, events=ev)
+        return x
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            self.step(i)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+    def time_kernels(self, steps, hip):
+        """Average duration (ms) per launch of each kernel, from the library's event
+        records around its launches on the stream."""
+        torch = self.torch
+        nk = len(self.kernels)
+        nb = len(self.blocks)
+        evs = hip.create(steps * nb * (nk + 1))
+        per = [evs[j * (nk + 1):(j + 1) * (nk + 1)] for j in range(steps * nb)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self.step(i, events=per[i * nb:(i + 1) * nb])
+        torch.cuda.synchronize()
+        tot = {k: 0.0 for k in self.kernels}
+        for ev in per:
+            for ki, k in enumerate(self.kernels):
+                tot[k] += hip.elapsed_ms(ev[ki], ev[ki + 1])
+        hip.destroy(evs)
+        return {k: v / (steps * nb) for k, v in tot.items()}
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "shifted_window_attention_roll_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get("entries", {}).get(f"{workload}:{kernel}")
+    if not ent or ent.get("source_digest") != source_digest():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def roofline(runner, kern_ms):
+    case = runner.case
+    work = stage_work(case)
+    dom = max(kern_ms, key=lambda k: kern_ms[k])
+    flops, nbytes = work[dom]
+    peak_f = PEAK_TFLOPS[case.dtype]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    sec = kern_ms[dom] * 1e-3
+    if flops / nbytes >= ridge:
+        ach = flops / sec / 1e12
+        r = {"bound": "mfma", "achieved": ach, "peak": peak_f, "unit": "TFLOP/s"}
+    else:
+        ach = nbytes / sec / 1e9
+        r = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = measured_traffic(dom, runner.name)
+    r["kernel"] = dom
+    r["kernel_ms"] = kern_ms[dom]
+    r["algorithmic_flops"] = flops
+    r["algorithmic_bytes"] = nbytes
+    return r
+
+
+def cpu_baseline(name, budget_s=15.0):
+    """The float64 oracle as it stands, on the first images of the workload."""
+    import numpy as np
+    import workloads
+    from oracle import swin_oracle as so
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    case = workloads.make_workload(name)
+
+    def run(nimg):
+        x = workloads.f64(case.x[:nimg])
+        t0 = time.perf_counter()
+        for blk in case.blocks:
+            table = (workloads.f64(blk.table) if case.mode == "v1" else
+                     so.cpb_table(workloads.f64(blk.cpb_w1), workloads.f64(blk.cpb_b1),
+                                  workloads.f64(blk.cpb_w2), workloads.f64(blk.cpb_b2), case.M))
+            x = so.wmsa_forward(x, workloads.f64(blk.w_qkv), workloads.f64(blk.b_qkv),
+                                workloads.f64(blk.w_proj), workloads.f64(blk.b_proj), table,
+                                case.M, blk.s, case.heads, case.mode,
+                                tau=None if blk.tau is None else workloads.f64(blk.tau))
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    nimg = int(max(1, min(case.B, budget_s / max(t1, 1e-3))))
+    t = run(nimg) if nimg > 1 else t1
+    tokens = nimg * case.H * case.W * len(case.blocks)
+    return {"value": tokens / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nimg} of {case.B} images of {name}, all {len(case.blocks)} block(s), "
+                      f"{tokens} block-tokens in {t:.2f} s (float64 numpy, BLAS threads={threads})"}
+
+
+def measure(name, steps, warmup, hip):
+    r = Runner(name)
+    ms = r.time_steps(steps, warmup)
+    kern = r.time_kernels(min(steps, 20), hip)
+    tok_s = r.tokens_per_step / (ms * 1e-3)
+    tflops = r.flops_per_step / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[r.case.dtype]
+    out = {"tokens_per_s": tok_s, "ms_per_step": ms, "tflops": tflops,
+           "mfma_peak_tflops": peak, "frac_of_mfma_peak": tflops / peak,
+           "kernel_ms": kern, "roofline": roofline(r, kern),
+           "tokens_per_step": r.tokens_per_step, "buffer_copies": r.copies}
+    del r
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=MAIN)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every window is independent; sharding is described in DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import shifted_window_attention_roll_amd as swin
+    import workloads
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    swin.load_library()
+    hip = HipEvents()
+
+    log(f"timing {args.workload}: warmup {args.warmup}, steps {args.steps}")
+    main_res = measure(args.workload, args.steps, args.warmup, hip)
+    log(json.dumps({"workload": args.workload, **{k: main_res[k] for k in
+                                                  ("tokens_per_s", "ms_per_step", "tflops",
+                                                   "kernel_ms")}}))
+    others = {}
+    if not args.no_others:
+        for name in workloads.WORKLOADS:
+            if name == args.workload:
+                continue
+            log(f"timing {name}")
+            res = measure(name, min(args.steps, 20), 3, hip)
+            others[name] = {k: res[k] for k in ("tokens_per_s", "ms_per_step", "tflops",
+                                                "frac_of_mfma_peak", "kernel_ms", "roofline")}
+            log(json.dumps({"workload": name, **others[name]}))
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        cpu = cpu_baseline(args.workload)
+        log(json.dumps(cpu))
+
+    case = workloads.make_workload(args.workload, B=1)
+    w = workloads.WORKLOADS[args.workload]
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": w["B"], "H": w["H"], "W": w["W"],
+                   "C": w["C"], "heads": w["heads"], "window": w["M"],
+                   "shifts": list(w["shifts"]), "mode": w["mode"],
+                   "tokens_per_step": main_res["tokens_per_step"], "parallelism": "none"},
+        "tflops": main_res["tflops"],
+        "frac_of_mfma_peak": main_res["frac_of_mfma_peak"],
+        "kernel_ms": main_res["kernel_ms"],
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "workloads": others,
+        "source_digest": source_digest(),
+    }
+    del case
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,7 +37,7 @@ typedef enum {
   SWIN_ERR_NULL = 1,        /* a required pointer is NULL                          */
   SWIN_ERR_SHAPE = 2,       /* sizes inconsistent (H % M, W % M, s range, C % heads) */
   SWIN_ERR_DTYPE = 3,       /* unknown dtype or mode value                         */
-  SWIN_ERR_UNSUPPORTED = 4, /* valid but not implemented (head dim != 32, M > 32)   */
+  SWIN_ERR_UNSUPPORTED = 4, /* valid but not implemented (head dim != 32, large M) */
   SWIN_ERR_ALIAS = 5,       /* an output overlaps an input or the workspace        */
   SWIN_ERR_WORKSPACE = 6,   /* workspace smaller than swin_wmsa_workspace_size()   */
   SWIN_ERR_ALIGN = 7,       /* a pointer is not 16-byte aligned                    */
@@ -137,12 +137,35 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d);
  *   concatenated, projected, and written back at the un-shifted position.
  * Computes in float32 for SWIN_F32; for SWIN_F16 / SWIN_BF16 the products run on
  * 16-bit matrix cores with float32 accumulation and float32 softmax.
- * Requires C/heads == 32 and M <= 32 (else SWIN_ERR_UNSUPPORTED).
+ * Requires C/heads == 32 and M <= 24 (16-bit) or M <= 16 (float32), else
+ * SWIN_ERR_UNSUPPORTED.
  */
 swin_status swin_wmsa_fwd(const swin_wmsa_desc* desc, const void* x, const void* w_qkv,
                           const void* b_qkv, const void* w_proj, const void* b_proj,
                           const float* bias_table, const float* tau, void* y,
                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Number of kernels swin_wmsa_fwd enqueues for this descriptor (0 if invalid or
+ * B == 0), and the function name (no namespace or template arguments) of the
+ * i-th one, as profilers print it inside the full name (NULL if out of range).
+ * Lets a profiler match per-kernel traces to the stages of the forward.
+ */
+int swin_wmsa_kernel_count(const swin_wmsa_desc* d);
+const char* swin_wmsa_kernel_name(const swin_wmsa_desc* d, int i);
+
+/*
+ * swin_wmsa_fwd plus per-kernel timing: records events[0] on `stream` before the
+ * first kernel and events[i+1] right after the i-th kernel.  `events` holds
+ * n_events caller-created hipEvent_t handles (passed as void*), n_events >=
+ * swin_wmsa_kernel_count(desc) + 1, else SWIN_ERR_SHAPE.  Same arguments,
+ * validation and results as swin_wmsa_fwd (page citations there).
+ */
+swin_status swin_wmsa_fwd_timed(const swin_wmsa_desc* desc, const void* x, const void* w_qkv,
+                                const void* b_qkv, const void* w_proj, const void* b_proj,
+                                const float* bias_table, const float* tau, void* y,
+                                void* workspace, size_t ws_bytes, void* stream,
+                                void* const* events, int n_events);
 
 #ifdef __cplusplus
 }

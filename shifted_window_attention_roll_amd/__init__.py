@@ -20,7 +20,8 @@ SWIN_OK = 0
 SWIN_V1, SWIN_V2 = 1, 2
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _EXPORTS = ("swin_status_str", "swin_abi_version", "swin_partition_shift", "swin_reverse_unshift",
-            "swin_cpb_table", "swin_wmsa_workspace_size", "swin_wmsa_fwd")
+            "swin_cpb_table", "swin_wmsa_workspace_size", "swin_wmsa_fwd",
+            "swin_wmsa_kernel_count", "swin_wmsa_kernel_name", "swin_wmsa_fwd_timed")
 
 
 class SwinDesc(ctypes.Structure):
@@ -58,6 +59,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swin_wmsa_fwd.restype = st
     lib.swin_wmsa_fwd.argtypes = [ctypes.POINTER(SwinDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   ctypes.c_size_t, vp]
+    lib.swin_wmsa_fwd_timed.restype = st
+    lib.swin_wmsa_fwd_timed.argtypes = [ctypes.POINTER(SwinDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, ctypes.c_size_t, vp, ctypes.POINTER(vp), i]
+    lib.swin_wmsa_kernel_count.restype = i
+    lib.swin_wmsa_kernel_count.argtypes = [ctypes.POINTER(SwinDesc)]
+    lib.swin_wmsa_kernel_name.restype = ctypes.c_char_p
+    lib.swin_wmsa_kernel_name.argtypes = [ctypes.POINTER(SwinDesc), i]
     _lib = lib
     return lib
 
@@ -133,24 +141,40 @@ def cpb_table(w1, b1, w2, b2, M: int, coord_scale: float = 0.0,
     return out
 
 
+def kernel_names(desc: SwinDesc):
+    """Function names of the kernels the forward enqueues, in launch order."""
+    lib = load_library()
+    n = lib.swin_wmsa_kernel_count(ctypes.byref(desc))
+    return [lib.swin_wmsa_kernel_name(ctypes.byref(desc), i).decode() for i in range(n)]
+
+
 def wmsa_fwd(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv: Optional[torch.Tensor],
              w_proj: torch.Tensor, b_proj: Optional[torch.Tensor], bias_table: torch.Tensor,
              M: int, s: int, heads: int, mode: str = "v1", tau: Optional[torch.Tensor] = None,
              scale: float = 0.0, tau_min: float = 0.0, out: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Shifted-window MHSA block forward; y has the shape and dtype of x."""
+             workspace: Optional[torch.Tensor] = None, stream=None,
+             events=None) -> torch.Tensor:
+    """Shifted-window MHSA block forward; y has the shape and dtype of x.
+
+    ``events``: optional sequence of raw hipEvent_t handles (ints), one more than
+    the number of kernels; the library records them around each kernel."""
     B, H, W, C = x.shape
     desc = make_desc(B, H, W, C, heads, M, s, mode, x.dtype, scale, tau_min)
     if out is None:
         out = torch.empty_like(x)
     if workspace is None:
         workspace = torch.empty(max(workspace_size(desc), 1), dtype=torch.uint8, device=x.device)
-    _check(load_library().swin_wmsa_fwd(
-        ctypes.byref(desc), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj), _ptr(b_proj),
-        _ptr(bias_table), _ptr(tau), _ptr(out), _ptr(workspace), workspace.numel(),
-        _stream(stream)))
+    args = (ctypes.byref(desc), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj), _ptr(b_proj),
+            _ptr(bias_table), _ptr(tau), _ptr(out), _ptr(workspace), workspace.numel(),
+            _stream(stream))
+    lib = load_library()
+    if events is None:
+        _check(lib.swin_wmsa_fwd(*args))
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check(lib.swin_wmsa_fwd_timed(*args, arr, len(events)))
     return out
 
 
 __all__ = ["load_library", "make_desc", "workspace_size", "partition_shift", "reverse_unshift",
-           "cpb_table", "wmsa_fwd", "SwinDesc", "SwinError", "LIB_PATH"]
+           "cpb_table", "wmsa_fwd", "kernel_names", "SwinDesc", "SwinError", "LIB_PATH"]

@@ -151,15 +151,35 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
   return ws_layout(d).total;
 }
 
-swin_status swin_wmsa_fwd(const swin_wmsa_desc* d, const void* x, const void* w_qkv,
-                          const void* b_qkv, const void* w_proj, const void* b_proj,
-                          const float* bias_table, const float* tau, void* y, void* workspace,
-                          size_t ws_bytes, void* stream) {
+static const char* const kStageNames[] = {"qkv_gemm_kernel", "window_attn_kernel",
+                                            "proj_gemm_kernel"};
+constexpr int kStages = 3;
+
+int swin_wmsa_kernel_count(const swin_wmsa_desc* d) {
+  if (validate_desc(d) != SWIN_OK || d->B == 0) return 0;
+  return kStages;
+}
+
+const char* swin_wmsa_kernel_name(const swin_wmsa_desc* d, int i) {
+  if (i < 0 || i >= swin_wmsa_kernel_count(d)) return nullptr;
+  return kStageNames[i];
+}
+
+static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const void* w_qkv,
+                                const void* b_qkv, const void* w_proj, const void* b_proj,
+                                const float* bias_table, const float* tau, void* y,
+                                void* workspace, size_t ws_bytes, void* stream,
+                                void* const* events, int n_events) {
   swin_status st = validate_desc(d);
   if (st != SWIN_OK) return st;
   if (d->B == 0) return SWIN_OK;
   if (!x || !w_qkv || !w_proj || !bias_table || !y || !workspace) return SWIN_ERR_NULL;
   if (d->mode == SWIN_V2 && !tau) return SWIN_ERR_NULL;
+  if (events) {
+    if (n_events < kStages + 1) return SWIN_ERR_SHAPE;
+    for (int i = 0; i <= kStages; ++i)
+      if (!events[i]) return SWIN_ERR_NULL;
+  }
   const WsLayout L = ws_layout(d);
   if (ws_bytes < L.total) return SWIN_ERR_WORKSPACE;
   const size_t e = elem_bytes(d->dtype);
@@ -198,10 +218,35 @@ swin_status swin_wmsa_fwd(const swin_wmsa_desc* d, const void* x, const void* w_
   p.buf.v = ws + L.v;
   p.buf.o = ws + L.o;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipError_t err = launch_qkv_gemm(p, hs);
+  auto mark = [&](int i) -> hipError_t {
+    return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
+  };
+  hipError_t err = mark(0);
+  if (err == hipSuccess) err = launch_qkv_gemm(p, hs);
+  if (err == hipSuccess) err = mark(1);
   if (err == hipSuccess) err = launch_window_attn(p, hs);
+  if (err == hipSuccess) err = mark(2);
   if (err == hipSuccess) err = launch_proj_gemm(p, hs);
+  if (err == hipSuccess) err = mark(3);
   return from_hip(err);
+}
+
+swin_status swin_wmsa_fwd(const swin_wmsa_desc* d, const void* x, const void* w_qkv,
+                          const void* b_qkv, const void* w_proj, const void* b_proj,
+                          const float* bias_table, const float* tau, void* y, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  return wmsa_forward(d, x, w_qkv, b_qkv, w_proj, b_proj, bias_table, tau, y, workspace,
+                      ws_bytes, stream, nullptr, 0);
+}
+
+swin_status swin_wmsa_fwd_timed(const swin_wmsa_desc* d, const void* x, const void* w_qkv,
+                                const void* b_qkv, const void* w_proj, const void* b_proj,
+                                const float* bias_table, const float* tau, void* y,
+                                void* workspace, size_t ws_bytes, void* stream,
+                                void* const* events, int n_events) {
+  if (!events) return SWIN_ERR_NULL;
+  return wmsa_forward(d, x, w_qkv, b_qkv, w_proj, b_proj, bias_table, tau, y, workspace,
+                      ws_bytes, stream, events, n_events);
 }
 
 }  // extern "C"

@@ -118,3 +118,19 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 7, 7, 32)
     with pytest.raises(ValueError):
         swin.partition_shift(x, 7, 3)
+
+
+def test_kernel_names_and_timed_rejects(lib):
+    d = _desc()
+    assert swin.kernel_names(d) == ["qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"]
+    assert lib.swin_wmsa_kernel_count(ctypes.byref(_desc(H=50))) == 0
+    assert lib.swin_wmsa_kernel_name(ctypes.byref(d), 3) is None
+    small = _desc(B=1, H=7, W=7, C=32, heads=1, M=7, s=3)
+    ws = lib.swin_wmsa_workspace_size(ctypes.byref(small))
+    ev = (ctypes.c_void_p * 4)(FAKE * 64, FAKE * 65, FAKE * 66, FAKE * 67)
+    args = (ctypes.byref(small), FAKE, FAKE * 2, None, FAKE * 3, None, FAKE * 4, None, FAKE * 8,
+            FAKE * 16, ws, None)
+    assert lib.swin_wmsa_fwd_timed(*args, None, 4) == NULL
+    assert lib.swin_wmsa_fwd_timed(*args, ev, 3) == SHAPE
+    ev_null = (ctypes.c_void_p * 4)(FAKE * 64, None, FAKE * 66, FAKE * 67)
+    assert lib.swin_wmsa_fwd_timed(*args, ev_null, 4) == NULL
