@@ -52,14 +52,15 @@ def flops_per_token(C, N):
 
 
 def stage_work(case):
-    """Algorithmic (flops, bytes) per launch of each kernel of the three-kernel
-    forward: the data its interface must move once (activations in and out, the
-    weights and the bias table), not what it re-reads."""
+    """Algorithmic (flops, bytes) per launch of each kernel: the data its
+    interface must move once (activations in and out, the weights and the bias
+    table), not what it re-reads."""
     T, C, N, heads = case.tokens, case.C, case.M * case.M, case.heads
     e = ELEM[case.dtype]
     eqk = 2 if (case.mode == "v2" and case.dtype != "fp32") else e
     tab = (2 * case.M - 1) ** 2 * heads * 4
     return {
+        "fused_small_kernel": ((8 * C * C + 4 * N * C) * T, T * 2 * C * e + 4 * C * C * e + tab),
         "qkv_gemm_kernel": (6 * C * C * T, T * (C * e + 2 * C * eqk + C * e) + 3 * C * C * e),
         "window_attn_kernel": (4 * N * C * T, T * (2 * C * eqk + C * e + C * e) + tab),
         "proj_gemm_kernel": (2 * C * C * T, T * 2 * C * e + C * C * e),

@@ -3,7 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/swin_wmsa.h"
+#include "swin_wmsa.h"
 #include "launch.hpp"
 
 using namespace swin;
@@ -53,11 +53,22 @@ int qk_type(const swin_wmsa_desc* d) {
   return d->dtype == SWIN_F16 ? kF16 : kBF16;
 }
 
+// Kernel plan: one fused kernel for small windows with few heads, else the
+// QKV GEMM -> window attention -> projection GEMM sequence through the workspace.
+enum Plan { kPlanFusedSmall = 0, kPlanThree = 1 };
+
+Plan choose_plan(const swin_wmsa_desc* d) {
+  const int heads = d->heads;
+  return (d->M * d->M <= 64 && heads <= 4 && d->C == kHeadDim * heads) ? kPlanFusedSmall
+                                                                       : kPlanThree;
+}
+
 struct WsLayout {
   size_t q, k, v, o, total;
 };
 
 WsLayout ws_layout(const swin_wmsa_desc* d) {
+  if (choose_plan(d) == kPlanFusedSmall) return WsLayout{0, 0, 0, 0, 0};
   const size_t tokens = (size_t)d->B * d->H * d->W;
   const size_t e = elem_bytes(d->dtype);
   const size_t eq = qk_type(d) == kF32 ? 4 : 2;
@@ -151,18 +162,20 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
   return ws_layout(d).total;
 }
 
-static const char* const kStageNames[] = {"qkv_gemm_kernel", "window_attn_kernel",
-                                            "proj_gemm_kernel"};
-constexpr int kStages = 3;
+static const char* const kPlanKernels[2][3] = {
+    {"fused_small_kernel", nullptr, nullptr},
+    {"qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"}};
+static const int kPlanCount[2] = {1, 3};
+constexpr int kMaxStages = 3;
 
 int swin_wmsa_kernel_count(const swin_wmsa_desc* d) {
   if (validate_desc(d) != SWIN_OK || d->B == 0) return 0;
-  return kStages;
+  return kPlanCount[choose_plan(d)];
 }
 
 const char* swin_wmsa_kernel_name(const swin_wmsa_desc* d, int i) {
   if (i < 0 || i >= swin_wmsa_kernel_count(d)) return nullptr;
-  return kStageNames[i];
+  return kPlanKernels[choose_plan(d)][i];
 }
 
 static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const void* w_qkv,
@@ -173,14 +186,17 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
   swin_status st = validate_desc(d);
   if (st != SWIN_OK) return st;
   if (d->B == 0) return SWIN_OK;
-  if (!x || !w_qkv || !w_proj || !bias_table || !y || !workspace) return SWIN_ERR_NULL;
+  const Plan plan = choose_plan(d);
+  const int stages = kPlanCount[plan];
+  const WsLayout L = ws_layout(d);
+  if (!x || !w_qkv || !w_proj || !bias_table || !y) return SWIN_ERR_NULL;
+  if (L.total > 0 && !workspace) return SWIN_ERR_NULL;
   if (d->mode == SWIN_V2 && !tau) return SWIN_ERR_NULL;
   if (events) {
-    if (n_events < kStages + 1) return SWIN_ERR_SHAPE;
-    for (int i = 0; i <= kStages; ++i)
+    if (n_events < stages + 1) return SWIN_ERR_SHAPE;
+    for (int i = 0; i <= stages; ++i)
       if (!events[i]) return SWIN_ERR_NULL;
   }
-  const WsLayout L = ws_layout(d);
   if (ws_bytes < L.total) return SWIN_ERR_WORKSPACE;
   const size_t e = elem_bytes(d->dtype);
   const size_t act = (size_t)d->B * d->H * d->W * d->C * e;
@@ -191,7 +207,7 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
       overlap(workspace, L.total, w_proj, C * C * e))
     return SWIN_ERR_ALIAS;
   if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(w_proj) || !aligned16(y) ||
-      !aligned16(workspace))
+      (L.total > 0 && !aligned16(workspace)))
     return SWIN_ERR_ALIGN;
 
   FwdParams p;
@@ -222,6 +238,11 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
   };
   hipError_t err = mark(0);
+  if (plan == kPlanFusedSmall) {
+    if (err == hipSuccess) err = launch_fused_small(p, hs);
+    if (err == hipSuccess) err = mark(1);
+    return from_hip(err);
+  }
   if (err == hipSuccess) err = launch_qkv_gemm(p, hs);
   if (err == hipSuccess) err = mark(1);
   if (err == hipSuccess) err = launch_window_attn(p, hs);

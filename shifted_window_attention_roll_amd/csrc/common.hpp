@@ -65,6 +65,31 @@ __device__ __forceinline__ T from_f32(float v) { return (T)v; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Butterfly steps across the four 16-lane rows of a wave on the VALU
+// (v_permlane16_swap / v_permlane32_swap): each call returns, in every lane, the
+// sum or max of the lane's value and that of lane l^16 (resp. l^32); both
+// partners get the identical result.
+__device__ __forceinline__ float xor16_sum(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
 // Window geometry.  Window w = b*nW + wy*nWx + wx, token t = ty*M + tx; the
 // slot holds shifted-frame (wy*M+ty, wx*M+tx), i.e. original position
 // ((wy*M+ty+s) mod H, (wx*M+tx+s) mod W).

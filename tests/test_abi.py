@@ -52,14 +52,19 @@ def _desc(**kw):
 
 
 def test_workspace_size(lib):
-    d = _desc()
-    T = 2 * 56 * 56
-    assert swin.workspace_size(d) >= 4 * T * 96 * 2
+    # small windows with <= 4 heads run as one fused kernel: no workspace
+    assert swin.workspace_size(_desc()) == 0
+    d = _desc(H=64, W=64, C=128, heads=4, M=16, s=8)
+    T = 2 * 64 * 64
+    assert swin.workspace_size(d) >= 4 * T * 128 * 2
     assert swin.workspace_size(_desc(B=0)) == 0
     assert swin.workspace_size(_desc(H=50)) == 0          # invalid -> 0
     # V2 with bf16 keeps q and k in float16: same byte count as bf16
-    assert swin.workspace_size(_desc(mode="v2", dtype=torch.bfloat16)) == swin.workspace_size(d)
-    assert swin.workspace_size(_desc(dtype=torch.float32)) >= 4 * T * 96 * 4
+    assert swin.workspace_size(swin.make_desc(2, 64, 64, 128, 4, 16, 8, "v2", torch.bfloat16)) == \
+        swin.workspace_size(d)
+    d32 = swin.make_desc(2, 64, 64, 128, 4, 16, 8, "v1", torch.float32)
+    assert swin.workspace_size(d32) >= 4 * T * 128 * 4
+    assert swin.workspace_size(_desc(C=512, heads=16)) >= 4 * 2 * 56 * 56 * 512 * 2
 
 
 FAKE = 1 << 20  # host-side stand-in addresses; validation fails before any use
@@ -73,7 +78,7 @@ def _fwd(lib, d, x=FAKE, wq=FAKE * 2, wp=FAKE * 3, tab=FAKE * 4, tau=FAKE * 5, y
 
 
 def test_fwd_rejects_before_launch(lib):
-    small = _desc(B=1, H=7, W=7, C=32, heads=1, M=7, s=3)
+    small = _desc(B=1, H=16, W=16, C=32, heads=1, M=16, s=3)
     assert _fwd(lib, _desc(H=50)) == SHAPE                   # H % M
     assert _fwd(lib, _desc(s=7)) == SHAPE                    # s >= M
     assert _fwd(lib, _desc(s=-1)) == SHAPE
@@ -86,7 +91,7 @@ def test_fwd_rejects_before_launch(lib):
     assert _fwd(lib, _desc(B=0)) == OK                        # empty: nothing to do
     assert _fwd(lib, small, x=None) == NULL
     assert _fwd(lib, small, tab=None) == NULL
-    assert _fwd(lib, _desc(B=1, H=7, W=7, C=32, heads=1, M=7, s=3, mode="v2"), tau=None) == NULL
+    assert _fwd(lib, _desc(B=1, H=16, W=16, C=32, heads=1, M=16, s=3, mode="v2"), tau=None) == NULL
     assert _fwd(lib, small, ws_bytes=16) == WS
     assert _fwd(lib, small, y=FAKE + 64) == ALIAS             # y overlaps x
     assert _fwd(lib, small, ws=FAKE * 8 + 128) == ALIAS       # workspace overlaps y
@@ -121,11 +126,14 @@ def test_binding_refuses_cpu_tensors(lib):
 
 
 def test_kernel_names_and_timed_rejects(lib):
-    d = _desc()
+    d = _desc(H=64, W=64, C=128, heads=4, M=16, s=8)
     assert swin.kernel_names(d) == ["qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"]
+    assert swin.kernel_names(_desc()) == ["fused_small_kernel"]
+    assert swin.kernel_names(_desc(C=512, heads=16)) == ["qkv_gemm_kernel", "window_attn_kernel",
+                                                          "proj_gemm_kernel"]
     assert lib.swin_wmsa_kernel_count(ctypes.byref(_desc(H=50))) == 0
     assert lib.swin_wmsa_kernel_name(ctypes.byref(d), 3) is None
-    small = _desc(B=1, H=7, W=7, C=32, heads=1, M=7, s=3)
+    small = _desc(B=1, H=16, W=16, C=32, heads=1, M=16, s=3)
     ws = lib.swin_wmsa_workspace_size(ctypes.byref(small))
     ev = (ctypes.c_void_p * 4)(FAKE * 64, FAKE * 65, FAKE * 66, FAKE * 67)
     args = (ctypes.byref(small), FAKE, FAKE * 2, None, FAKE * 3, None, FAKE * 4, None, FAKE * 8,
