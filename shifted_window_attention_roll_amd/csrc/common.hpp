@@ -31,6 +31,43 @@ __device__ __forceinline__ vec8<T> load8(const T* p) {
   }
 }
 
+// Global-memory (address space 1) 16-byte loads / stores.  Pointers that travel
+// through a kernel-argument struct or inline-asm laundering lose their address
+// space, and the generic (flat) instructions the compiler then emits also count
+// against the LDS wait counter; these keep them on the global path.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+typedef const __attribute__((address_space(1))) u32x4* cg16;
+typedef __attribute__((address_space(1))) u32x4* g16;
+
+__device__ __forceinline__ uint4 gload16(const void* p) {
+  return __builtin_bit_cast(uint4, *(cg16)(p));
+}
+__device__ __forceinline__ void gstore16(void* p, uint4 v) {
+  *(g16)(p) = __builtin_bit_cast(u32x4, v);
+}
+
+template <typename T>
+__device__ __forceinline__ vec8<T> gload8(gptr<T> p) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(vec8<T>, *(cg16)p);
+  } else {
+    struct P { u32x4 a, b; } pr{*(cg16)p, *(cg16)(p + 4)};
+    return __builtin_bit_cast(vec8<T>, pr);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ vec8<T> gload8(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(vec8<T>, gload16(p));
+  } else {
+    struct P { uint4 a, b; } pr{gload16(p), gload16(p + 4)};
+    return __builtin_bit_cast(vec8<T>, pr);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const vec8<T>& v) {
   if constexpr (sizeof(T) == 2) {

@@ -78,7 +78,8 @@ void fused_window_kernel(FwdParams p, int n_windows) {
 
   const Geom g = p.g;
   const int N = g.N, M = g.M;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int g4 = lane >> 4, i16 = lane & 15;
   const int n2 = 2 * M - 1;
   const int nrel = n2 * n2;
@@ -120,7 +121,7 @@ void fused_window_kernel(FwdParams p, int n_windows) {
       const T* row = x + (ok ? src_row(wpos, tok_yx[j]) * C : 0) + g4 * 8;
 #pragma unroll
       for (int k = 0; k < HEADS; ++k) {
-        xf[j][k] = ok ? load8(row + k * 32) : vec8<T>{};
+        xf[j][k] = ok ? gload8(row + k * 32) : vec8<T>{};
       }
     }
   };
@@ -164,14 +165,14 @@ void fused_window_kernel(FwdParams p, int n_windows) {
     }
   __syncthreads();
 
-  auto wfrag = [&](const T* base, int row, int k) {
-    return load8(base + (uint32_t)(row * C + k * 32 + g4 * 8));
+  auto wfrag = [&](gptr<T> base, int row, int k) {
+    return gload8(base + (uint32_t)(row * C + k * 32 + g4 * 8));
   };
 
   for (; w < n_windows; w += gridDim.x) {
     const WinPos wpos = win_pos(w);
-    const T* wqi = wq;
-    const T* wpi = wp;
+    gptr<T> wqi = (gptr<T>)wq;
+    gptr<T> wpi = (gptr<T>)wp;
     asm volatile("" : "+s"(wqi), "+s"(wpi));  // keep the weight loads in the loop
 
     // ---- phase 1: QKV blocks (p, h) = (q|k|v, head) -----------------------------
@@ -333,8 +334,8 @@ void fused_window_kernel(FwdParams p, int n_windows) {
       if (slot_yx[k] < 0) continue;
       const int i = tid + k * NT;
       const int c = i % CPR;
-      *reinterpret_cast<uint4*>(y + src_row(wpos, slot_yx[k]) * C + c * EPC) =
-          *reinterpret_cast<const uint4*>(&ks[(i / CPR) * LDQ + c * EPC]);
+      gstore16(y + src_row(wpos, slot_yx[k]) * C + c * EPC,
+               *reinterpret_cast<const uint4*>(&ks[(i / CPR) * LDQ + c * EPC]));
     }
     __syncthreads();  // staging read before the next window's phase 1 writes K
   }
