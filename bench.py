@@ -60,7 +60,7 @@ def stage_work(case):
     eqk = 2 if (case.mode == "v2" and case.dtype != "fp32") else e
     tab = (2 * case.M - 1) ** 2 * heads * 4
     return {
-        "fused_small_kernel": ((8 * C * C + 4 * N * C) * T, T * 2 * C * e + 4 * C * C * e + tab),
+        "fused_window_kernel": ((8 * C * C + 4 * N * C) * T, T * 2 * C * e + 4 * C * C * e + tab),
         "qkv_gemm_kernel": (6 * C * C * T, T * (C * e + 2 * C * eqk + C * e) + 3 * C * C * e),
         "window_attn_kernel": (4 * N * C * T, T * (2 * C * eqk + C * e + C * e) + tab),
         "proj_gemm_kernel": (2 * C * C * T, T * 2 * C * e + C * C * e),
@@ -246,11 +246,15 @@ def cpu_baseline(name, budget_s=15.0):
 
     t1 = run(1)
     nimg = int(max(1, min(case.B, budget_s / max(t1, 1e-3))))
-    t = run(nimg) if nimg > 1 else t1
-    tokens = nimg * case.H * case.W * len(case.blocks)
+    t, passes = 0.0, 0
+    while passes == 0 or (t < 0.66 * budget_s and passes < 100):
+        t += run(nimg)
+        passes += 1
+    tokens = passes * nimg * case.H * case.W * len(case.blocks)
     return {"value": tokens / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{nimg} of {case.B} images of {name}, all {len(case.blocks)} block(s), "
-                      f"{tokens} block-tokens in {t:.2f} s (float64 numpy, BLAS threads={threads})"}
+            "sample": f"{passes} pass(es) over {nimg} of {case.B} images of {name}, all "
+                      f"{len(case.blocks)} block(s), {tokens} block-tokens in {t:.2f} s "
+                      f"(float64 numpy, BLAS threads={threads})"}
 
 
 def measure(name, steps, warmup, hip):
@@ -268,6 +272,106 @@ def measure(name, steps, warmup, hip):
     return out
 
 
+CALIB_BYTES = 256 << 20   # size of the plain device copy that calibrates the HBM counters
+CALIB_REPS = 4
+
+
+def traffic_run(name, steps):
+    """Workload steps followed by CALIB_REPS plain device-to-device copies of
+    CALIB_BYTES, for two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE)."""
+    import torch
+    import shifted_window_attention_roll_amd as swin
+    swin.load_library()
+    r = Runner(name)
+    for i in range(steps):
+        r.step(i)
+    torch.cuda.synchronize()
+    src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(CALIB_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"traffic run done: {name}, {steps} steps, {CALIB_REPS} x {CALIB_BYTES} B copies")
+
+
+def _counter_rows(d):
+    import csv
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def _per_kernel_kib(rows, counter, kernels):
+    """Average counter value (KiB per dispatch) of each named kernel, and the
+    per-copy value of the calibration copies (the copy dispatches issued after
+    the last workload kernel)."""
+    per = {}
+    sums = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        did, k, v = int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])
+        sums.setdefault((did, k), 0.0)
+        sums[(did, k)] += v          # a counter may come as several per-XCD rows
+    last = max([d for (d, k) in sums if any(n in k for n in kernels)] or [0])
+    calib = [v for (d, k), v in sums.items() if d > last and "copyBuffer" in k]
+    for n in kernels:
+        vals = [v for (d, k), v in sums.items() if n in k]
+        if vals:
+            per[n] = (sum(vals) / len(vals), len(vals))
+    return per, (sum(calib) / CALIB_REPS if calib else None), len(calib)
+
+
+def traffic_summarize(name, fetch_dir, write_dir, command):
+    """Scale the FETCH_SIZE / WRITE_SIZE counters by what they read for a plain
+    copy of known size and store bytes per launch of each kernel."""
+    import shifted_window_attention_roll_amd as swin
+    import workloads
+    case = workloads.make_workload(name, B=1)
+    desc = swin.make_desc(case.B, case.H, case.W, case.C, case.heads, case.M,
+                          case.blocks[0].s, case.mode, case.torch_dtype)
+    kernels = swin.kernel_names(desc)
+    fk, fcal, nfc = _per_kernel_kib(_counter_rows(fetch_dir), "FETCH_SIZE", kernels)
+    wk, wcal, nwc = _per_kernel_kib(_counter_rows(write_dir), "WRITE_SIZE", kernels)
+    if not fcal or not wcal:
+        raise SystemExit("calibration copies not found in the counter output")
+    fscale = CALIB_BYTES / (fcal * 1024.0)
+    wscale = CALIB_BYTES / (wcal * 1024.0)
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    rec = {"entries": {}}
+    if os.path.exists(path):
+        with open(path) as f:
+            rec = json.load(f)
+    full = workloads.make_workload(name)
+    lines = [f"# HBM traffic per launch, {name}", "",
+             f"Command: `{command}`", "",
+             f"Calibration: {CALIB_REPS} device copies of {CALIB_BYTES} B; FETCH_SIZE reads "
+             f"{fcal:.1f} KiB per copy (scale {fscale:.4f}), WRITE_SIZE {wcal:.1f} KiB "
+             f"(scale {wscale:.4f}).", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes/launch | "
+             "algorithmic bytes/launch | ratio |", "|---|---|---|---|---|---|---|"]
+    work = stage_work(full)
+    for k in kernels:
+        if k not in fk or k not in wk:
+            continue
+        b = fk[k][0] * 1024.0 * fscale + wk[k][0] * 1024.0 * wscale
+        alg = work[k][1]
+        rec["entries"][f"{name}:{k}"] = {
+            "fetch_kib": fk[k][0], "write_kib": wk[k][0], "fetch_scale": fscale,
+            "write_scale": wscale, "bytes_per_launch": b, "algorithmic_bytes": alg,
+            "source_digest": source_digest(), "command": command}
+        lines.append(f"| {k} | {fk[k][1]} | {fk[k][0]:.1f} | {wk[k][0]:.1f} | {b:.4g} | "
+                     f"{alg:.4g} | {b / alg:.3f} |")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -276,7 +380,15 @@ def main():
     ap.add_argument("--workload", default=MAIN)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="run --steps steps and the counter calibration copies, print no JSON")
+    ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc outputs into profiles/hbm_traffic.json")
+    ap.add_argument("--traffic-command", default="", help="command recorded with the summary")
     args = ap.parse_args()
+    if args.traffic_summarize:
+        traffic_summarize(args.workload, *args.traffic_summarize, args.traffic_command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -290,6 +402,9 @@ def main():
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     swin.load_library()
+    if args.traffic_run:
+        traffic_run(args.workload, args.steps)
+        return
     hip = HipEvents()
 
     log(f"timing {args.workload}: warmup {args.warmup}, steps {args.steps}")

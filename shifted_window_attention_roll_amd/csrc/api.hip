@@ -163,7 +163,7 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
 }
 
 static const char* const kPlanKernels[2][3] = {
-    {"fused_small_kernel", nullptr, nullptr},
+    {"fused_window_kernel", nullptr, nullptr},
     {"qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"}};
 static const int kPlanCount[2] = {1, 3};
 constexpr int kMaxStages = 3;
@@ -239,7 +239,7 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
   };
   hipError_t err = mark(0);
   if (plan == kPlanFusedSmall) {
-    if (err == hipSuccess) err = launch_fused_small(p, hs);
+    if (err == hipSuccess) err = launch_fused_window(p, hs);
     if (err == hipSuccess) err = mark(1);
     return from_hip(err);
   }

@@ -379,7 +379,7 @@ hipError_t launch_mode(const FwdParams& p, int cus, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_fused_small(const FwdParams& p, hipStream_t st) {
+hipError_t launch_fused_window(const FwdParams& p, hipStream_t st) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

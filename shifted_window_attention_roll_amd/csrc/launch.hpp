@@ -50,7 +50,7 @@ hipError_t launch_qkv_gemm(const FwdParams& p, hipStream_t st);
 hipError_t launch_window_attn(const FwdParams& p, hipStream_t st);
 hipError_t launch_proj_gemm(const FwdParams& p, hipStream_t st);
 // Single-kernel forward for N <= 64 and C = 32 * heads with heads <= 4.
-hipError_t launch_fused_small(const FwdParams& p, hipStream_t st);
+hipError_t launch_fused_window(const FwdParams& p, hipStream_t st);
 
 // Largest window side the attention kernel stages in LDS for an element size.
 inline int max_window(int io_bytes) { return io_bytes == 4 ? 16 : 24; }

@@ -128,7 +128,7 @@ def test_binding_refuses_cpu_tensors(lib):
 def test_kernel_names_and_timed_rejects(lib):
     d = _desc(H=64, W=64, C=128, heads=4, M=16, s=8)
     assert swin.kernel_names(d) == ["qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"]
-    assert swin.kernel_names(_desc()) == ["fused_small_kernel"]
+    assert swin.kernel_names(_desc()) == ["fused_window_kernel"]
     assert swin.kernel_names(_desc(C=512, heads=16)) == ["qkv_gemm_kernel", "window_attn_kernel",
                                                           "proj_gemm_kernel"]
     assert lib.swin_wmsa_kernel_count(ctypes.byref(_desc(H=50))) == 0
