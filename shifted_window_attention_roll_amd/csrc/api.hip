@@ -39,6 +39,7 @@ Geom make_geom(int B, int H, int W, int C, int M, int s, int heads) {
   g.nW = (H / M) * (W / M);
   g.N = M * M;
   g.heads = heads;
+  g.chunked = 0;
   return g;
 }
 
@@ -53,14 +54,21 @@ int qk_type(const swin_wmsa_desc* d) {
   return d->dtype == SWIN_F16 ? kF16 : kBF16;
 }
 
-// Kernel plan: one fused kernel for small windows with few heads, else the
-// QKV GEMM -> window attention -> projection GEMM sequence through the workspace.
-enum Plan { kPlanFusedSmall = 0, kPlanThree = 1 };
+// Kernel plan: one fused kernel for small windows with few heads; else the
+// QKV GEMM -> window attention -> projection GEMM sequence through the
+// workspace, with the tiled attention (chunked slots, V^T) for 16-bit I/O and
+// window sides 8, 16, 24.
+enum Plan { kPlanFusedSmall = 0, kPlanThree = 1, kPlanTiled = 2 };
+
+int io_type(const swin_wmsa_desc* d) {
+  return d->dtype == SWIN_F32 ? kF32 : d->dtype == SWIN_F16 ? kF16 : kBF16;
+}
 
 Plan choose_plan(const swin_wmsa_desc* d) {
   const int heads = d->heads;
-  return (d->M * d->M <= 64 && heads <= 4 && d->C == kHeadDim * heads) ? kPlanFusedSmall
-                                                                       : kPlanThree;
+  if (d->M * d->M <= 64 && heads <= 4 && d->C == kHeadDim * heads) return kPlanFusedSmall;
+  if (tiled_attn_supported(d->M, io_type(d))) return kPlanTiled;
+  return kPlanThree;
 }
 
 struct WsLayout {
@@ -162,10 +170,11 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
   return ws_layout(d).total;
 }
 
-static const char* const kPlanKernels[2][3] = {
+static const char* const kPlanKernels[3][3] = {
     {"fused_window_kernel", nullptr, nullptr},
-    {"qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"}};
-static const int kPlanCount[2] = {1, 3};
+    {"qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"},
+    {"qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"}};
+static const int kPlanCount[3] = {1, 3, 3};
 constexpr int kMaxStages = 3;
 
 int swin_wmsa_kernel_count(const swin_wmsa_desc* d) {
@@ -213,7 +222,8 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
   FwdParams p;
   memset(&p, 0, sizeof(p));
   p.g = make_geom(d->B, d->H, d->W, d->C, d->M, d->s, d->heads);
-  p.io = d->dtype == SWIN_F32 ? kF32 : d->dtype == SWIN_F16 ? kF16 : kBF16;
+  p.io = io_type(d);
+  p.g.chunked = plan == kPlanTiled ? 1 : 0;
   p.qk = qk_type(d);
   p.v2 = d->mode == SWIN_V2;
   const float scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)kHeadDim);
@@ -245,7 +255,8 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
   }
   if (err == hipSuccess) err = launch_qkv_gemm(p, hs);
   if (err == hipSuccess) err = mark(1);
-  if (err == hipSuccess) err = launch_window_attn(p, hs);
+  if (err == hipSuccess)
+    err = plan == kPlanTiled ? launch_tiled_attn(p, hs) : launch_window_attn(p, hs);
   if (err == hipSuccess) err = mark(2);
   if (err == hipSuccess) err = launch_proj_gemm(p, hs);
   if (err == hipSuccess) err = mark(3);

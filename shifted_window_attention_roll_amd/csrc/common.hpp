@@ -127,12 +127,32 @@ __device__ __forceinline__ float xor32_max(float v) {
   return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
-// Window geometry.  Window w = b*nW + wy*nWx + wx, token t = ty*M + tx; the
-// slot holds shifted-frame (wy*M+ty, wx*M+tx), i.e. original position
-// ((wy*M+ty+s) mod H, (wx*M+tx+s) mod W).
+// Window geometry.  Window w = b*nW + wy*nWx + wx; slot t of the window holds
+// window-local (ty, tx), i.e. shifted-frame (wy*M+ty, wx*M+tx), i.e. original
+// position ((wy*M+ty+s) mod H, (wx*M+tx+s) mod W).  Slots are row-major
+// (t = ty*M + tx) unless `chunked`: for M % 8 == 0 the window is cut into
+// column chunks 8 tokens wide, and t = cx*8M + ty*8 + (tx - 8cx) with cx = tx/8,
+// so that every 8 consecutive slots are 8 consecutive tokens of one window row
+// and every 16 consecutive slots are a 2 x 8 patch.  Attention does not depend
+// on the order of the tokens inside a window; the order only has to be the
+// same where the slots are written and where they are read back.
 struct Geom {
   int B, H, W, C, M, s, nWx, nW, N, heads;
+  int chunked;
 };
+
+__device__ __forceinline__ void slot_yx(const Geom& g, int t, int& ty, int& tx) {
+  if (g.chunked) {
+    const int cs = 8 * g.M;
+    const int cx = t / cs;
+    const int rem = t - cx * cs;
+    ty = rem >> 3;
+    tx = 8 * cx + (rem & 7);
+  } else {
+    ty = t / g.M;
+    tx = t - ty * g.M;
+  }
+}
 
 __device__ __forceinline__ int64_t src_token(const Geom& g, int r) {
   int w = r / g.N;
@@ -141,8 +161,8 @@ __device__ __forceinline__ int64_t src_token(const Geom& g, int r) {
   int wl = w - b * g.nW;
   int wy = wl / g.nWx;
   int wx = wl - wy * g.nWx;
-  int ty = t / g.M;
-  int tx = t - ty * g.M;
+  int ty, tx;
+  slot_yx(g, t, ty, tx);
   int y = wy * g.M + ty + g.s;
   if (y >= g.H) y -= g.H;
   int x = wx * g.M + tx + g.s;

@@ -49,6 +49,10 @@ hipError_t launch_cpb_table(const float* w1, const float* b1, const float* w2, c
 hipError_t launch_qkv_gemm(const FwdParams& p, hipStream_t st);
 hipError_t launch_window_attn(const FwdParams& p, hipStream_t st);
 hipError_t launch_proj_gemm(const FwdParams& p, hipStream_t st);
+// Attention for window sides 8, 16, 24 with 16-bit I/O; needs chunked slots
+// and V^T in the workspace (see Geom and the QKV GEMM).
+bool tiled_attn_supported(int M, int io);
+hipError_t launch_tiled_attn(const FwdParams& p, hipStream_t st);
 // Single-kernel forward for N <= 64 and C = 32 * heads with heads <= 4.
 hipError_t launch_fused_window(const FwdParams& p, hipStream_t st);
 

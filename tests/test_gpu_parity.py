@@ -93,6 +93,12 @@ SMALL = [
     (2, 8, 8, 96, 3, 8, 4, "fp32", "v1", 0.1),
     (1, 12, 12, 32, 1, 6, 5, "bf16", "v2", 0.1),
     (1, 10, 10, 32, 1, 5, 2, "fp32", "v2", 0.1),     # N = 25: a single padded key block
+    # tiled attention (16-bit, M in 8 / 16 / 24); the split M - s inside a chunk
+    (2, 16, 24, 256, 8, 8, 3, "fp16", "v1", 0.1),    # split 5: inside chunk 0
+    (1, 32, 48, 64, 2, 16, 5, "bf16", "v2", 0.1),    # split 11: inside chunk 1
+    (2, 48, 24, 96, 3, 24, 7, "fp16", "v2", 0.1),    # split 17: inside chunk 2
+    (1, 16, 16, 32, 1, 16, 8, "bf16", "v1", 0.3),    # window = image, shifted
+    (1, 24, 48, 160, 5, 8, 0, "bf16", "v2", 0.1),    # no shift
 ]
 
 
