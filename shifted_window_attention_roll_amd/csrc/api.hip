@@ -40,6 +40,11 @@ Geom make_geom(int B, int H, int W, int C, int M, int s, int heads) {
   g.N = M * M;
   g.heads = heads;
   g.chunked = 0;
+  g.dN = make_fastdiv(g.N);
+  g.dnW = make_fastdiv(g.nW);
+  g.dnWx = make_fastdiv(g.nWx);
+  g.dM = make_fastdiv(M);
+  g.dChunk = make_fastdiv(8 * M);
   return g;
 }
 
@@ -69,6 +74,11 @@ Plan choose_plan(const swin_wmsa_desc* d) {
   if (d->M * d->M <= 64 && heads <= 4 && d->C == kHeadDim * heads) return kPlanFusedSmall;
   if (tiled_attn_supported(d->M, io_type(d))) return kPlanTiled;
   return kPlanThree;
+}
+
+bool use_tiled_gemm(const swin_wmsa_desc* d) {
+  const size_t bytes = (size_t)d->B * d->H * d->W * d->C * elem_bytes(d->dtype);
+  return tiled_gemm_supported(d->C, io_type(d)) && bytes < ((size_t)1 << 31);
 }
 
 struct WsLayout {
@@ -170,11 +180,16 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
   return ws_layout(d).total;
 }
 
-static const char* const kPlanKernels[3][3] = {
-    {"fused_window_kernel", nullptr, nullptr},
-    {"qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"},
-    {"qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"}};
 static const int kPlanCount[3] = {1, 3, 3};
+
+static const char* stage_name(const swin_wmsa_desc* d, int i) {
+  const Plan plan = choose_plan(d);
+  if (plan == kPlanFusedSmall) return "fused_window_kernel";
+  const bool tg = use_tiled_gemm(d);
+  if (i == 0) return tg ? "qkv_tiled_kernel" : "qkv_gemm_kernel";
+  if (i == 1) return plan == kPlanTiled ? "tiled_attn_kernel" : "window_attn_kernel";
+  return tg ? "proj_tiled_kernel" : "proj_gemm_kernel";
+}
 constexpr int kMaxStages = 3;
 
 int swin_wmsa_kernel_count(const swin_wmsa_desc* d) {
@@ -184,7 +199,7 @@ int swin_wmsa_kernel_count(const swin_wmsa_desc* d) {
 
 const char* swin_wmsa_kernel_name(const swin_wmsa_desc* d, int i) {
   if (i < 0 || i >= swin_wmsa_kernel_count(d)) return nullptr;
-  return kPlanKernels[choose_plan(d)][i];
+  return stage_name(d, i);
 }
 
 static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const void* w_qkv,
@@ -253,12 +268,13 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
     if (err == hipSuccess) err = mark(1);
     return from_hip(err);
   }
-  if (err == hipSuccess) err = launch_qkv_gemm(p, hs);
+  const bool tg = use_tiled_gemm(d);
+  if (err == hipSuccess) err = tg ? launch_qkv_tiled(p, hs) : launch_qkv_gemm(p, hs);
   if (err == hipSuccess) err = mark(1);
   if (err == hipSuccess)
     err = plan == kPlanTiled ? launch_tiled_attn(p, hs) : launch_window_attn(p, hs);
   if (err == hipSuccess) err = mark(2);
-  if (err == hipSuccess) err = launch_proj_gemm(p, hs);
+  if (err == hipSuccess) err = tg ? launch_proj_tiled(p, hs) : launch_proj_gemm(p, hs);
   if (err == hipSuccess) err = mark(3);
   return from_hip(err);
 }

@@ -136,30 +136,62 @@ __device__ __forceinline__ float xor32_max(float v) {
 // and every 16 consecutive slots are a 2 x 8 patch.  Attention does not depend
 // on the order of the tokens inside a window; the order only has to be the
 // same where the slots are written and where they are read back.
+// Division of 32-bit unsigned n by a divisor d fixed at launch: one high
+// multiply, a subtract, an add and two shifts (round-up multiplier method of
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): with l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d)
+// + 1, n / d = (t + ((n - t) >> 1)) >> (l - 1) where t = umulhi(m, n), exact
+// for every n < 2^32.
+struct FastDiv {
+  uint32_t d, m, s1, s2;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.d = d;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  f.s1 = l > 0 ? 1 : 0;
+  f.s2 = l > 0 ? l - 1 : 0;
+  return f;
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  const uint32_t t = __umulhi(n, f.m);
+  return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
 struct Geom {
   int B, H, W, C, M, s, nWx, nW, N, heads;
   int chunked;
+  FastDiv dN, dnW, dnWx, dM, dChunk;  // N, nW, nWx, M, 8M
 };
 
 __device__ __forceinline__ void slot_yx(const Geom& g, int t, int& ty, int& tx) {
   if (g.chunked) {
-    const int cs = 8 * g.M;
-    const int cx = t / cs;
-    const int rem = t - cx * cs;
+    const int cx = (int)fdiv((uint32_t)t, g.dChunk);
+    const int rem = t - cx * 8 * g.M;
     ty = rem >> 3;
     tx = 8 * cx + (rem & 7);
   } else {
-    ty = t / g.M;
+    ty = (int)fdiv((uint32_t)t, g.dM);
     tx = t - ty * g.M;
   }
 }
 
+// Window w and slot t of window-order row r.
+__device__ __forceinline__ void row_wt(const Geom& g, int r, int& w, int& t) {
+  w = (int)fdiv((uint32_t)r, g.dN);
+  t = r - w * g.N;
+}
+
 __device__ __forceinline__ int64_t src_token(const Geom& g, int r) {
-  int w = r / g.N;
-  int t = r - w * g.N;
-  int b = w / g.nW;
+  int w, t;
+  row_wt(g, r, w, t);
+  int b = (int)fdiv((uint32_t)w, g.dnW);
   int wl = w - b * g.nW;
-  int wy = wl / g.nWx;
+  int wy = (int)fdiv((uint32_t)wl, g.dnWx);
   int wx = wl - wy * g.nWx;
   int ty, tx;
   slot_yx(g, t, ty, tx);

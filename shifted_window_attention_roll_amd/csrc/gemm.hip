@@ -10,8 +10,8 @@
 // contiguous on both sides).  The QKV GEMM reads its A rows through the cyclic
 // shift + window partition map (each row is one contiguous token vector in x),
 // and stores q, k, v per (window, head) block, so the attention kernel reads
-// contiguous [N, 32] tiles (v as [32, N], i.e. V^T, with chunked slots).  The
-// projection GEMM writes each window-order row back to its un-shifted position.
+// contiguous [N, 32] tiles.  The projection GEMM writes each window-order row
+// back to its un-shifted position.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -180,11 +180,8 @@ __global__ __launch_bounds__(kThreads) void qkv_gemm_kernel(FwdParams p) {
             static_cast<QT*>(p.buf.q)[base + 16 * jj] = from_f32<QT>(v);
           else if (part == 1)
             static_cast<QT*>(p.buf.k)[base + 16 * jj] = from_f32<QT>(v);
-          else if (!g.chunked)
+          else
             static_cast<T*>(p.buf.v)[base + 16 * jj] = from_f32<T>(v);
-          else  // V^T per (window, head): [32][N]
-            static_cast<T*>(p.buf.v)[((int64_t)(w * g.heads + h) * 32 + (lane & 15) + 16 * jj) *
-                                         g.N + t] = from_f32<T>(v);
         }
       }
   }

@@ -1,0 +1,519 @@
+// QKV and output projection GEMMs for 16-bit I/O and C a multiple of 128: large
+// output tiles on the matrix cores, operands streamed global -> LDS by
+// direct-to-LDS loads into a double buffer.
+//
+// "Boost Vision Transformer with GPU-Friendly Sparsity and Quantization",
+// Section 3.2 / Figure 3: Q/K/V and the output projection are GEMMs.
+// "Boosting Swin Transformer Speed", Inference Optimization (GEMM with its bias
+// fused, no separate transposes) and Training Optimization (shift / partition /
+// reverse folded into the neighbouring ops): the A rows of the QKV GEMM are
+// gathered from x through the cyclic shift + window partition map, and the
+// projection stores each row at its un-shifted token position.
+//
+// Tile BM x BN, K in stages of 64 (128 bytes per row).  Each wave instruction
+// of `global_load_lds_dwordx4` fills 1 KB of LDS = 8 rows of a stage; lane L
+// lands at row L/8, 16-byte slot L%8, and fetches source chunk
+// (L%8) ^ (row%8), so that a stage row holds its eight chunks XOR-swizzled and
+// the 16 rows of a matrix-core fragment read conflict-free.
+//
+// Persistent workgroups, one per CU, walk their tiles as one continuous
+// sequence of stages, so the loads of the next tile's first stages overlap the
+// current tile's last stages and its epilogue.  Two LDS buffers: the loads of
+// stage s+2 go out mid-stage s (after the barrier that publishes stage s+1),
+// and the A rows of stage s+4 are touched with a 4-byte load per row so that
+// they are in L2 by the time their stage is loaded.  Workgroups reach the 8
+// XCDs (each with its own L2) round-robin; every XCD walks a contiguous range
+// of tiles, column tiles fastest, so the workgroups running together on one
+// XCD share their A rows, and A is read from HBM about once.
+//
+// Orientation.  The products are formed as C^T (the weight fragment is the
+// MFMA's A operand) with the weight rows of each pair of 16-channel tiles
+// interleaved, so a lane holds 8 consecutive channels of one token: one
+// 16-byte store, and V2 normalises a head with a 4-lane reduction.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace swin {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_vptr;
+
+constexpr int kStageK = 64;
+constexpr int kPrefetch = 4;  // stages ahead for the L2 touch of A
+
+template <int BM, int BN, int WGM, int WGN>
+struct Cfg {
+  static constexpr int WAVES = WGM * WGN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_INS = BM / 8 / WAVES;  // 1 KB wave instructions per stage
+  static constexpr int B_INS = BN / 8 / WAVES;
+  static constexpr int SMEM = 2 * STAGE + 4 * WAVES * 64;  // + touch-load sink
+  static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "load split");
+  static_assert(WM % 16 == 0 && WN % 32 == 0, "wave tile");
+};
+
+// vmcnt(n) and lgkmcnt(0): all but the last n global loads of this wave have
+// landed, and so have all of its LDS reads (gfx9 encoding: vmcnt low bits
+// [3:0] and high bits [15:14], expcnt [6:4] left at 7, lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Source byte offsets of one tile for this lane (stage 0): its A load rows
+// (gathered: one offset per row; linear: row i adds i * 8 rows, folded into
+// the scalar offset), its first B load row (the others follow linearly) and
+// the A row it touches for L2.  Rows past the end of A read zeros (the buffer
+// resource's bound).
+template <int AI, bool LINEAR>
+struct TileSrc {
+  uint32_t a[LINEAR ? 1 : AI], b, touch;
+};
+
+// Row r of a stage is filled by wave instruction r / 8, lane 8*(r%8) + slot;
+// the lane fetches chunk (L%8) ^ (L/8), i.e. (slot) ^ (row % 8).
+template <int INS>
+__device__ __forceinline__ int load_row(int i) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave * INS + i) * 8 + (lane >> 3);
+}
+__device__ __forceinline__ uint32_t load_chunk_bytes() {
+  const int lane = threadIdx.x & 63;
+  return (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);
+}
+
+// Tiles of this workgroup: XCD x = id % 8 owns the contiguous range
+// [x*per + min(x, rem), ...) of the row-major tile order; its workgroups take
+// every (workgroups on x)-th tile of the range.
+struct TileWalk {
+  int first, stride, count;
+};
+__device__ __forceinline__ TileWalk tile_walk(int ntiles) {
+  const int G = gridDim.x, id = blockIdx.x;
+  const int nx = G < 8 ? G : 8;
+  const int x = id % nx, j = id / nx;
+  const int wpx = (G - x + nx - 1) / nx;  // workgroups on XCD x
+  const int per = ntiles / nx, rem = ntiles % nx;
+  const int start = x * per + min(x, rem), cnt = per + (x < rem ? 1 : 0);
+  TileWalk t;
+  t.first = start + j;
+  t.stride = wpx;
+  t.count = j < cnt ? (cnt - j + wpx - 1) / wpx : 0;
+  return t;
+}
+
+// The persistent main loop.  src(tile, TileSrc&) fills the source offsets of a
+// tile, epi(tile, acc) consumes its accumulators.  acc[i][j] covers token tile
+// i x channel tile j in C^T form; the weight rows of each pair of channel
+// tiles are interleaved so that lane l holds token 16i + l%16 and channels
+// 32(j/2) + 8(l/16) + 4(j%2) + r: 8 consecutive channels, one 16-byte store.
+template <typename T, int BM, int BN, int WGM, int WGN, int NK, bool LINEAR, class SrcFn,
+          class EpiFn>
+__device__ __forceinline__ void run_tiles(const char* __restrict__ A, uint32_t a_bytes,
+                                          const char* __restrict__ Bw, uint32_t b_bytes,
+                                          uint32_t rowbytes, char* smem, int ntiles, SrcFn src,
+                                          EpiFn epi) {
+  using G = Cfg<BM, BN, WGM, WGN>;
+  using Src = TileSrc<G::A_INS, LINEAR>;
+  static_assert(NK % 2 == 0 && NK >= kPrefetch, "stage parity and touch distance");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave - (wave / WGN) * WGN;
+  const TileWalk tw = tile_walk(ntiles);
+  if (tw.count <= 0) return;
+  char* sink = smem + 2 * G::STAGE + wave * 256;
+
+  // Buffer resources (raw, bounds = the whole tensor): the lane offset is a
+  // 32-bit VGPR, the stage offset a scalar, so a load costs no vector ALU.
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(A), (short)0, (int)a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rbw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bw), (short)0, (int)b_bytes, 0x00020000);
+  auto dma = [&](const Src& sr, int buf, int k) {
+    char* sa = smem + buf * G::STAGE;
+    char* sb = sa + G::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < G::A_INS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_vptr)(sa + (wave * G::A_INS + i) * 1024), 16, sr.a[LINEAR ? 0 : i],
+          k * (kStageK * 2) + (LINEAR ? i * 8 * rowbytes : 0), 0, 0);
+#pragma unroll
+    for (int i = 0; i < G::B_INS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbw, (lds_vptr)(sb + (wave * G::B_INS + i) * 1024),
+                                               16, sr.b, k * (kStageK * 2) + i * 8 * rowbytes, 0,
+                                               0);
+  };
+  // One 4-byte load per A row of stage k: the line lands in L2 (and a
+  // throw-away LDS sink); nothing reads it.
+  auto touch = [&](const Src& sr, int k) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)sink, 4, sr.touch, k * (kStageK * 2),
+                                             0, 0);
+  };
+
+  // Fragment lane offsets inside a 32-row pair of tiles: row (t = tile parity)
+  // 16t + l%16 for the token rows, 8(l%16 / 4) + 4t + l%4 for the weight rows
+  // (they become the MFMA output rows); 16-byte chunk 4kk + l/16, swizzled by
+  // row % 8.
+  const int i16 = lane & 15, g4 = lane >> 4;
+  auto lane_off = [&](bool perm, int t, int kk) -> uint32_t {
+    const int row = perm ? 8 * (i16 >> 2) + 4 * t + (i16 & 3) : 16 * t + i16;
+    return (uint32_t)row * 128 + ((uint32_t)((4 * kk + g4) ^ (row & 7)) << 4);
+  };
+  uint32_t offa[2][2], offb[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      offa[t][kk] = lane_off(false, t, kk);
+      offb[t][kk] = lane_off(true, t, kk);
+    }
+  auto stage_a = [&](int buf) { return smem + buf * G::STAGE + wm * G::WM * 128; };
+  auto stage_b = [&](int buf) { return smem + buf * G::STAGE + G::A_BYTES + wn * G::WN * 128; };
+  auto read_frags = [&](int buf, int kk, vec8<T>(&af)[G::TM], vec8<T>(&bf)[G::TN]) {
+    const char* sa = stage_a(buf);
+    const char* sb = stage_b(buf);
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+      af[i] = *reinterpret_cast<const vec8<T>*>(sa + (i >> 1) * 4096 + offa[i & 1][kk]);
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j)
+      bf[j] = *reinterpret_cast<const vec8<T>*>(sb + (j >> 1) * 4096 + offb[j & 1][kk]);
+  };
+  f32x4 acc[G::TM][G::TN];
+  auto multiply = [&](const vec8<T>(&af)[G::TM], const vec8<T>(&bf)[G::TN]) {
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) acc[i][j] = mma_16x16x32(bf[j], af[i], acc[i][j]);
+  };
+
+  Src cur, nxt;
+  int tile = tw.first;
+  src(tile, cur);
+  src(tw.count > 1 ? tile + tw.stride : tile, nxt);
+  // Prologue: stage 0 and the touches of stages 2, 3; then stage 1.  The wait
+  // rule below (vmcnt(1)) relies on exactly one touch following every stage's
+  // loads.
+  dma(cur, 0, 0);
+  touch(cur, 2);
+  wait_vm<1>();
+  __syncthreads();
+  vec8<T> af0[G::TM], bf0[G::TN], af1[G::TM], bf1[G::TN];
+  read_frags(0, 0, af0, bf0);
+  read_frags(0, 1, af1, bf1);
+  dma(cur, 1, 1);
+  touch(cur, 3);
+
+  for (int it = 0; it < tw.count; ++it) {
+    const bool more = it + 1 < tw.count;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(af0, bf0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<1>();  // this wave's loads of stage k+1 have landed
+      __syncthreads();  // ... everyone's; and buffer k%2 is free
+      // Loads of stage k+2 (this tile or the next), touch of stage k+4.
+      if (k + 2 < NK) dma(cur, k & 1, k + 2);
+      else if (more) dma(nxt, k & 1, k + 2 - NK);
+      if (k + kPrefetch < NK) touch(cur, k + kPrefetch);
+      else touch(more ? nxt : cur, more ? k + kPrefetch - NK : NK - 1);
+      if (k + 1 < NK) read_frags((k + 1) & 1, 0, af0, bf0);
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(af1, bf1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 1 < NK) read_frags((k + 1) & 1, 1, af1, bf1);
+    }
+    epi(tile, acc);
+    // The next tile's stage 0 (buffer 0) was published by the last barrier;
+    // its fragments are read after the epilogue so that they do not occupy
+    // registers during it (stale and unused after the last tile).
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, 0, af0, bf0);
+    read_frags(0, 1, af1, bf1);
+    tile += tw.stride;
+    cur = nxt;
+    if (it + 2 < tw.count) src(tile + tw.stride, nxt);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&v)[8], float m) {
+  vec8<T> o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(v[e] * m);
+  gstore16(p, __builtin_bit_cast(uint4, o));
+}
+
+// Eight consecutive linear-bias entries (element loads: the bias pointers
+// carry no alignment promise beyond the element size).
+template <typename T>
+__device__ __forceinline__ void load_bias8(const T* b, int c, float (&o)[8]) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r) o[r] = b ? (float)b[c + r] : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// QKV projection: rows are window slots (gathered from x), columns 0..3C.
+// ---------------------------------------------------------------------------
+template <typename T, typename QT, int BM, int BN, int WGM, int WGN, int NK>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void qkv_tiled_kernel(FwdParams p) {
+  using G = Cfg<BM, BN, WGM, WGN>;
+  using Src = TileSrc<G::A_INS, false>;
+  __shared__ __attribute__((aligned(1024))) char smem[G::SMEM];
+  const Geom& g = p.g;
+  const int rows = g.B * g.H * g.W;
+  const int C = g.C;
+  const int ncol = 3 * C / BN;
+  const int ntiles = (rows + BM - 1) / BM * ncol;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave - (wave / WGN) * WGN;
+  const int g4 = lane >> 4, i16 = lane & 15;
+  const uint32_t cb = load_chunk_bytes();
+  const uint32_t rowbytes = (uint32_t)C * 2;
+
+  auto src = [&](int tile, Src& sr) {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    const int m0 = rb * BM, n0 = cbk * BN;
+#pragma unroll
+    for (int i = 0; i < G::A_INS; ++i) {
+      const int r = min(m0 + load_row<G::A_INS>(i), rows - 1);
+      sr.a[i] = (uint32_t)src_token(g, r) * rowbytes + cb;
+    }
+    sr.b = (uint32_t)(n0 + load_row<G::B_INS>(0)) * rowbytes + cb;
+    sr.touch = (uint32_t)src_token(g, min(m0 + (int)threadIdx.x % BM, rows - 1)) * rowbytes;
+  };
+
+  const T* bq = static_cast<const T*>(p.b_qkv);
+  auto epi = [&](int tile, f32x4 (&acc)[G::TM][G::TN]) {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    const int m0 = rb * BM, n0 = cbk * BN;
+    const int part = n0 / C;            // 0 = q, 1 = k, 2 = v (BN divides C)
+    int c00 = n0 + wn * G::WN;  // first channel of this wave (a head start)
+    int rbase = m0 + wm * G::WM;
+    // Opaque here: keeps the epilogue's loads and row arithmetic from being
+    // scheduled into the main loop, where they would hold registers.
+    asm volatile("" : "+v"(rbase), "+s"(c00));
+    const int h0 = (c00 - part * C) >> 5;
+    constexpr int NH = G::TN / 2;
+    // All loads first: under the in-order memory counter a load issued after
+    // a store would make its wait cover that store too.
+    float bias[NH][8], qm[NH];
+#pragma unroll
+    for (int jh = 0; jh < NH; ++jh) {
+      load_bias8(bq, c00 + 32 * jh + 8 * g4, bias[jh]);
+      qm[jh] = part != 0 ? 1.0f
+                         : (p.v2 ? kLog2e / fmaxf(p.tau[h0 + jh], p.tau_min) : p.q_mult);
+    }
+    // lane: token 16i + i16; channels 32jh + 8 g4 + e of head h0 + jh.
+    const bool norm = p.v2 && part < 2;
+    const float eps2 = p.eps * p.eps;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      const int row = rbase + 16 * i + i16;
+      int w, t;
+      row_wt(g, row, w, t);
+      const bool ok = row < rows;
+      // Element offset of (item = w*heads + h0, slot t, dim 8 g4) in a
+      // [item][N][32] buffer; the next head adds N*32 (32-bit: tokens*C < 2^30).
+      const uint32_t off = ((uint32_t)(w * g.heads + h0) * (uint32_t)g.N + (uint32_t)t) * 32u +
+                           8u * (uint32_t)g4;
+#pragma unroll
+      for (int jh = 0; jh < NH; ++jh) {
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[i][2 * jh][r] + bias[jh][r];
+          v[4 + r] = acc[i][2 * jh + 1][r] + bias[jh][4 + r];
+        }
+        float mult = qm[jh];
+        if (norm) {
+          // "Swin Transformer V2" summary, How It Works: cosine similarity over
+          // tau (tau clipped at tau_min); 1/tau and log2(e) fold into q.
+          // 1 / max(|v|, eps) = rsqrt(max(|v|^2, eps^2)).
+          float ss = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+          ss = xor32_sum(xor16_sum(ss));
+          mult *= __builtin_amdgcn_rsqf(fmaxf(ss, eps2));
+        }
+        if (!ok) continue;
+        const uint32_t o = off + (uint32_t)jh * (uint32_t)g.N * 32u;
+        if (part < 2)
+          store8(static_cast<QT*>(part == 0 ? p.buf.q : p.buf.k) + o, v, mult);
+        else
+          store8(static_cast<T*>(p.buf.v) + o, v, 1.0f);
+      }
+    }
+  };
+  run_tiles<T, BM, BN, WGM, WGN, NK, false>(static_cast<const char*>(p.x),
+                                            (uint32_t)rows * rowbytes,
+                                            static_cast<const char*>(p.w_qkv), 3 * C * rowbytes,
+                                            rowbytes, smem, ntiles, src, epi);
+}
+
+// ---------------------------------------------------------------------------
+// Output projection: rows are window slots of O, stored at their token in y.
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int WGM, int WGN, int NK>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_tiled_kernel(FwdParams p) {
+  using G = Cfg<BM, BN, WGM, WGN>;
+  using Src = TileSrc<G::A_INS, true>;
+  __shared__ __attribute__((aligned(1024))) char smem[G::SMEM];
+  const Geom& g = p.g;
+  const int rows = g.B * g.H * g.W;
+  const int C = g.C;
+  const int ncol = C / BN;
+  const int ntiles = (rows + BM - 1) / BM * ncol;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave - (wave / WGN) * WGN;
+  const int g4 = lane >> 4, i16 = lane & 15;
+  const uint32_t cb = load_chunk_bytes();
+  const uint32_t rowbytes = (uint32_t)C * 2;
+
+  auto src = [&](int tile, Src& sr) {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    const int m0 = rb * BM, n0 = cbk * BN;
+    sr.a[0] = (uint32_t)(m0 + load_row<G::A_INS>(0)) * rowbytes + cb;
+    sr.b = (uint32_t)(n0 + load_row<G::B_INS>(0)) * rowbytes + cb;
+    sr.touch = (uint32_t)min(m0 + (int)threadIdx.x % BM, rows - 1) * rowbytes;
+  };
+  const T* bp = static_cast<const T*>(p.b_proj);
+  T* y = static_cast<T*>(p.y);
+  auto epi = [&](int tile, f32x4 (&acc)[G::TM][G::TN]) {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    const int m0 = rb * BM, n0 = cbk * BN;
+    int rbase = m0 + wm * G::WM + i16;
+    int c00 = n0 + wn * G::WN;
+    // Opaque here: keeps the epilogue's loads and row arithmetic from being
+    // scheduled into the main loop, where they would hold registers.
+    asm volatile("" : "+v"(rbase), "+s"(c00));
+    c00 += 8 * g4;
+    // Element offset of each row's un-shifted token (32-bit: tokens * C < 2^30).
+    uint32_t dst[G::TM];
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      const int row = rbase + 16 * i;
+      dst[i] = row < rows ? (uint32_t)src_token(g, row) * (uint32_t)C : 0xffffffffu;
+    }
+    // All loads before the first store (in-order memory counter).
+    float b[G::TN / 2][8];
+#pragma unroll
+    for (int jh = 0; jh < G::TN / 2; ++jh) load_bias8(bp, c00 + 32 * jh, b[jh]);
+    // lane: token 16i + i16; channels 32jh + 8 g4 + e.
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      if (dst[i] == 0xffffffffu) continue;
+#pragma unroll
+      for (int jh = 0; jh < G::TN / 2; ++jh) {
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[i][2 * jh][r] + b[jh][r];
+          v[4 + r] = acc[i][2 * jh + 1][r] + b[jh][4 + r];
+        }
+        store8(y + dst[i] + c00 + 32 * jh, v, 1.0f);
+      }
+    }
+  };
+  run_tiles<T, BM, BN, WGM, WGN, NK, true>(static_cast<const char*>(p.buf.o),
+                                           (uint32_t)rows * rowbytes,
+                                           static_cast<const char*>(p.w_proj), C * rowbytes,
+                                           rowbytes, smem, ntiles, src, epi);
+}
+
+int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+  }
+  return n;
+}
+
+int persistent_grid(int ntiles, int per_cu) {
+  return ntiles < per_cu * num_cus() ? ntiles : per_cu * num_cus();
+}
+
+// Tiles: 256 x 256 (2 x 2 waves of 128 x 128) when there are at least two per
+// CU; else 128 x 128 (2 x 2 waves of 64 x 64) so that small problems still
+// spread over the chip.  K = C in 64-wide stages.
+template <typename T, typename QT, int NK>
+void qkv_tiled_launch(const FwdParams& p, hipStream_t st) {
+  const int rows = p.g.B * p.g.H * p.g.W;
+  const int big = (rows + 255) / 256 * (3 * p.g.C / 256);
+  if (big >= 2 * num_cus()) {
+    hipLaunchKernelGGL((qkv_tiled_kernel<T, QT, 256, 256, 2, 2, NK>), dim3(persistent_grid(big, 1)),
+                       dim3(256), 0, st, p);
+  } else {
+    const int small = (rows + 127) / 128 * (3 * p.g.C / 128);
+    hipLaunchKernelGGL((qkv_tiled_kernel<T, QT, 128, 128, 2, 2, NK>),
+                       dim3(persistent_grid(small, 2)), dim3(256), 0, st, p);
+  }
+}
+
+template <typename T, typename QT>
+hipError_t qkv_tiled_dispatch(const FwdParams& p, hipStream_t st) {
+  switch (p.g.C) {
+    case 256: qkv_tiled_launch<T, QT, 4>(p, st); break;
+    case 512: qkv_tiled_launch<T, QT, 8>(p, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int NK>
+void proj_tiled_launch(const FwdParams& p, hipStream_t st) {
+  const int rows = p.g.B * p.g.H * p.g.W;
+  const int big = (rows + 255) / 256 * (p.g.C / 256);
+  if (big >= 2 * num_cus()) {
+    hipLaunchKernelGGL((proj_tiled_kernel<T, 256, 256, 2, 2, NK>), dim3(persistent_grid(big, 1)),
+                       dim3(256), 0, st, p);
+  } else {
+    const int small = (rows + 127) / 128 * (p.g.C / 128);
+    hipLaunchKernelGGL((proj_tiled_kernel<T, 128, 128, 2, 2, NK>), dim3(persistent_grid(small, 2)),
+                       dim3(256), 0, st, p);
+  }
+}
+
+template <typename T>
+hipError_t proj_tiled_dispatch(const FwdParams& p, hipStream_t st) {
+  switch (p.g.C) {
+    case 256: proj_tiled_launch<T, 4>(p, st); break;
+    case 512: proj_tiled_launch<T, 8>(p, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool tiled_gemm_supported(int C, int io) { return io != kF32 && (C == 256 || C == 512); }
+
+hipError_t launch_qkv_tiled(const FwdParams& p, hipStream_t st) {
+  if (!tiled_gemm_supported(p.g.C, p.io)) return hipErrorInvalidValue;
+  if (p.io == kF16) return qkv_tiled_dispatch<h16, h16>(p, st);
+  if (p.qk == kF16) return qkv_tiled_dispatch<b16, h16>(p, st);
+  return qkv_tiled_dispatch<b16, b16>(p, st);
+}
+
+hipError_t launch_proj_tiled(const FwdParams& p, hipStream_t st) {
+  if (!tiled_gemm_supported(p.g.C, p.io)) return hipErrorInvalidValue;
+  if (p.io == kF16) return proj_tiled_dispatch<h16>(p, st);
+  return proj_tiled_dispatch<b16>(p, st);
+}
+
+}  // namespace swin

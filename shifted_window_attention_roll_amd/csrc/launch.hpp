@@ -50,9 +50,14 @@ hipError_t launch_qkv_gemm(const FwdParams& p, hipStream_t st);
 hipError_t launch_window_attn(const FwdParams& p, hipStream_t st);
 hipError_t launch_proj_gemm(const FwdParams& p, hipStream_t st);
 // Attention for window sides 8, 16, 24 with 16-bit I/O; needs chunked slots
-// and V^T in the workspace (see Geom and the QKV GEMM).
+// (see Geom).
 bool tiled_attn_supported(int M, int io);
 hipError_t launch_tiled_attn(const FwdParams& p, hipStream_t st);
+// QKV / projection GEMMs for 16-bit I/O and C in {256, 512} (32-bit offsets:
+// tokens * C * 2 must stay below 2^31).
+bool tiled_gemm_supported(int C, int io);
+hipError_t launch_qkv_tiled(const FwdParams& p, hipStream_t st);
+hipError_t launch_proj_tiled(const FwdParams& p, hipStream_t st);
 // Single-kernel forward for N <= 64 and C = 32 * heads with heads <= 4.
 hipError_t launch_fused_window(const FwdParams& p, hipStream_t st);
 

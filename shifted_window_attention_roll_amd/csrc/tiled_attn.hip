@@ -11,8 +11,8 @@
 //
 // Slots are chunked (see Geom): 16 consecutive slots are a 2 x 8 patch of the
 // window and 32 consecutive slots a 4 x 8 patch.  Inputs per (window, head):
-// q, k as [N][32] and V^T as [32][N], q already scaled so that the logits are
-// in base 2.
+// q, k, v as [N][32], q already scaled so that the logits are in base 2; v is
+// transposed into V^T while it is staged in LDS.
 //
 // Register layout.  A wave owns QTL tiles of 16 queries.  S^T = K Q^T on the
 // matrix cores, with the K rows of each 32-key block permuted so that lane l
@@ -197,9 +197,12 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_attn_kernel(FwdParams p) {
     const int r = i >> 2, c = i & 3;
     *reinterpret_cast<uint4*>(&ks[r * LDK + c * 8]) = gload16(kg + i * 8);
   }
+  // V arrives as [N][32]; it is transposed into V^T on the way into LDS.
   for (int i = tid; i < N * D / 8; i += NT) {
-    const int r = i / (N / 8), c = i - r * (N / 8);
-    *reinterpret_cast<uint4*>(&vts[r * LDV + c * 8]) = gload16(vg + i * 8);
+    const int r = i >> 2, c = i & 3;
+    const vec8<VT> v = __builtin_bit_cast(vec8<VT>, gload16(vg + i * 8));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vts[(c * 8 + e) * LDV + r] = v[e];
   }
   // Table rows stored reversed, times log2(e); then 8 x -inf.
   for (int i = tid; i < R * R + 8; i += NT) {

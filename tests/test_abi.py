@@ -127,16 +127,21 @@ def test_binding_refuses_cpu_tensors(lib):
 
 def test_kernel_names_and_timed_rejects(lib):
     d = _desc(H=64, W=64, C=128, heads=4, M=16, s=8)
-    tiled = ["qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"]
+    tiled = ["qkv_tiled_kernel", "tiled_attn_kernel", "proj_tiled_kernel"]
     three = ["qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"]
-    assert swin.kernel_names(d) == tiled
+    assert swin.kernel_names(d) == ["qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"]
     assert swin.kernel_names(_desc(H=48, W=48, M=24, s=12, C=512, heads=16,
                                    dtype=torch.bfloat16)) == tiled
     assert swin.kernel_names(_desc(H=64, W=64, M=16, s=8, C=128, heads=4,
                                    dtype=torch.float32)) == three
     assert swin.kernel_names(_desc()) == ["fused_window_kernel"]
-    assert swin.kernel_names(_desc(C=512, heads=16)) == three
+    assert swin.kernel_names(_desc(C=512, heads=16)) == ["qkv_tiled_kernel", "window_attn_kernel",
+                                                          "proj_tiled_kernel"]
     assert swin.kernel_names(_desc(H=48, W=48, M=12, s=6, C=128, heads=4)) == three
+    assert swin.kernel_names(_desc(H=48, W=48, M=12, s=6, C=256, heads=8)) == [
+        "qkv_tiled_kernel", "window_attn_kernel", "proj_tiled_kernel"]
+    assert swin.kernel_names(_desc(H=48, W=48, M=16, s=6, C=96, heads=3)) == [
+        "qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"]
     assert lib.swin_wmsa_kernel_count(ctypes.byref(_desc(H=50))) == 0
     assert lib.swin_wmsa_kernel_name(ctypes.byref(d), 3) is None
     small = _desc(B=1, H=16, W=16, C=32, heads=1, M=16, s=3)
