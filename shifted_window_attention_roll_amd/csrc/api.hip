@@ -59,11 +59,11 @@ int qk_type(const swin_wmsa_desc* d) {
   return d->dtype == SWIN_F16 ? kF16 : kBF16;
 }
 
-// Kernel plan: one fused kernel for small windows with few heads; else the
-// QKV GEMM -> window attention -> projection GEMM sequence through the
-// workspace, with the tiled attention (chunked slots, V^T) for 16-bit I/O and
-// window sides 8, 16, 24.
-enum Plan { kPlanFusedSmall = 0, kPlanThree = 1, kPlanTiled = 2 };
+// Kernel plan: one fused kernel for small windows with few heads, and for
+// window side 16 with few heads and 16-bit I/O; else the QKV GEMM -> window
+// attention -> projection GEMM sequence through the workspace, with the tiled
+// attention (chunked slots) for 16-bit I/O and window sides 8, 16, 24.
+enum Plan { kPlanFusedSmall = 0, kPlanThree = 1, kPlanTiled = 2, kPlanFusedW16 = 3 };
 
 int io_type(const swin_wmsa_desc* d) {
   return d->dtype == SWIN_F32 ? kF32 : d->dtype == SWIN_F16 ? kF16 : kBF16;
@@ -72,6 +72,7 @@ int io_type(const swin_wmsa_desc* d) {
 Plan choose_plan(const swin_wmsa_desc* d) {
   const int heads = d->heads;
   if (d->M * d->M <= 64 && heads <= 4 && d->C == kHeadDim * heads) return kPlanFusedSmall;
+  if (fused_w16_supported(d->M, d->C, heads, io_type(d))) return kPlanFusedW16;
   if (tiled_attn_supported(d->M, io_type(d))) return kPlanTiled;
   return kPlanThree;
 }
@@ -86,7 +87,8 @@ struct WsLayout {
 };
 
 WsLayout ws_layout(const swin_wmsa_desc* d) {
-  if (choose_plan(d) == kPlanFusedSmall) return WsLayout{0, 0, 0, 0, 0};
+  const Plan plan = choose_plan(d);
+  if (plan == kPlanFusedSmall || plan == kPlanFusedW16) return WsLayout{0, 0, 0, 0, 0};
   const size_t tokens = (size_t)d->B * d->H * d->W;
   const size_t e = elem_bytes(d->dtype);
   const size_t eq = qk_type(d) == kF32 ? 4 : 2;
@@ -180,11 +182,12 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
   return ws_layout(d).total;
 }
 
-static const int kPlanCount[3] = {1, 3, 3};
+static const int kPlanCount[4] = {1, 3, 3, 1};
 
 static const char* stage_name(const swin_wmsa_desc* d, int i) {
   const Plan plan = choose_plan(d);
   if (plan == kPlanFusedSmall) return "fused_window_kernel";
+  if (plan == kPlanFusedW16) return "fused_w16_kernel";
   const bool tg = use_tiled_gemm(d);
   if (i == 0) return tg ? "qkv_tiled_kernel" : "qkv_gemm_kernel";
   if (i == 1) return plan == kPlanTiled ? "tiled_attn_kernel" : "window_attn_kernel";
@@ -238,7 +241,7 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
   memset(&p, 0, sizeof(p));
   p.g = make_geom(d->B, d->H, d->W, d->C, d->M, d->s, d->heads);
   p.io = io_type(d);
-  p.g.chunked = plan == kPlanTiled ? 1 : 0;
+  p.g.chunked = (plan == kPlanTiled || plan == kPlanFusedW16) ? 1 : 0;
   p.qk = qk_type(d);
   p.v2 = d->mode == SWIN_V2;
   const float scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)kHeadDim);
@@ -263,8 +266,9 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
   };
   hipError_t err = mark(0);
-  if (plan == kPlanFusedSmall) {
-    if (err == hipSuccess) err = launch_fused_window(p, hs);
+  if (plan == kPlanFusedSmall || plan == kPlanFusedW16) {
+    if (err == hipSuccess)
+      err = plan == kPlanFusedSmall ? launch_fused_window(p, hs) : launch_fused_w16(p, hs);
     if (err == hipSuccess) err = mark(1);
     return from_hip(err);
   }

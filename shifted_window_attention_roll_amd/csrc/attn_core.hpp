@@ -1,0 +1,283 @@
+// Attention core shared by the kernels whose window side M is a multiple of 8:
+// QTL tiles of 16 queries of one (window, head) against the window's N = M*M
+// keys, with K and V staged in LDS as [key][d] rows.
+//
+// Pages: "Boosting Swin Transformer Speed", Training Optimization (fused MHA:
+// softmax fused with the two products) and Inference Optimization (the bias
+// table is prepared once; the mask is index arithmetic); "Swin Transformer V2"
+// summary, How It Works (logit = similarity + relative position bias B_ij).
+//
+// Slots are chunked (see Geom): 16 consecutive slots are a 2 x 8 patch of the
+// window and 32 consecutive slots a 4 x 8 patch; tile T holds slots 16T..16T+15.
+//
+// Register layout.  S^T = K Q^T on the matrix cores, with the K rows of each
+// 32-key block permuted so that lane l receives query (l % 16) and the 8 keys
+// 8*(l/16) .. +7 of the block: one window row, 8 consecutive columns.  The
+// relative position index of those 8 keys then walks one row of the table
+// backwards, so with the rows of the table stored reversed the lane reads its
+// 8 biases from 8 consecutive floats (from one of four shifted copies of the
+// table, so that the read is two aligned 16-byte loads); they are the MFMA's
+// initial accumulator.  P stays in registers as the B operand of
+// O^T = V^T P^T; the V^T fragments come from transposing LDS reads
+// (ds_read_b64_tr_b16) with the head dims of each 16-row fragment pair
+// interleaved, so that lane l ends with O^T for d = 8*(l/16) .. +7 of its
+// query -- the B-operand slice of a following product with O, or one 16-byte
+// store.  Row sums come from one more MFMA (ones x P^T), i.e. from exactly the
+// rounded P that multiplies V.
+//
+// Softmax.  Base 2, online, with a lazy running max: a block only rescales when
+// some lane sees a logit more than G above the row's current reference, so the
+// exponentials stay below 2^G (G = 64 with bfloat16 P, whose exponent range is
+// that of float; 8 with float16 P).  Each key block runs in three phases over
+// all query tiles (logits, the rare rescale, exponentials and products), with
+// the next block's LDS operands loaded while the current one is computed.
+//
+// Shifted windows.  Only the last window row (column) of the grid mixes two
+// slices of the shifted frame, split at M - s; a pair is allowed when query and
+// key are on the same side in both directions.  A tile whose lanes have no
+// allowed key in a block skips it; otherwise the bias of a fully masked key
+// group is read from a row of -inf, and a group that straddles the split gets
+// -inf per key.
+#pragma once
+
+#include "common.hpp"
+
+namespace swin {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s;
+
+constexpr int kAttnLD = 40;  // LDS row pitch (elements) of staged K and V
+
+// Floats per copy of the reversed bias table (+ room so that every copy can
+// be read 8 floats past any start index it is used with).
+template <int M>
+constexpr int table_stride() { return ((2 * M - 1) * (2 * M - 1) + 8 + 3) / 4 * 4; }
+
+// Fills the 4 shifted copies of the head's reversed bias table (times log2 e):
+// copy c holds element i + c at position i, -inf past the end; table is
+// [(2M-1)^2, heads] float.
+template <int M>
+__device__ __forceinline__ void fill_bias_copies(float* rt4, const float* table, int heads, int h,
+                                                 int tid, int nthreads) {
+  constexpr int R = 2 * M - 1;
+  constexpr int TS = table_stride<M>();
+  for (int i = tid; i < 4 * TS; i += nthreads) {
+    const int c = i / TS, e = i - c * TS + c;
+    float v = -__builtin_inff();
+    if (e < R * R) {
+      const int r = e / R, cc = e - r * R;
+      v = table[(int64_t)(r * R + (R - 1 - cc)) * heads + h] * kLog2e;
+    }
+    rt4[i] = v;
+  }
+}
+
+// V^T fragment pair t (t = 0, 1) of keys kb .. kb+31 from V stored as [key][d]
+// rows of kAttnLD elements, by two transposing LDS reads.  Within each 16-lane
+// group g, lane (4a + b) of the read receives element b of the 8-byte chunk
+// addressed by lane 4e + a, for e = 0..3; lane s of group g addresses
+// V[kb + 8g + 4h + s/4][8(s%4) + 4t] (h = read 0 or 1), so lane i = 4a + b gets
+// V[kb + 8g + 4h + e][8a + 4t + b]: row i of fragment t is head dim
+// 8a + 4t + b, its k-slice the keys 8g .. 8g+7.
+// vl: this lane's address for kb = 0, t = 0, h = 0.
+template <typename VT>
+__device__ __forceinline__ vec8<VT> vt_frag(lds_v4s vl, int kb, int t) {
+  const lds_v4s p0 = vl + (kb * kAttnLD + 4 * t) / 4;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0 + kAttnLD);
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(vec8<VT>, both);
+}
+
+// Attention of query tiles tile[0..QTL) (q fragments qf: lane l holds query
+// 16*tile + l%16, d = 8*(l/16) .. +7, pre-scaled to base-2 logits) against all
+// N keys.  ks, vs: K and V as [N][kAttnLD]; rt4: the 4 bias copies; ninf: 8 x
+// -inf (16-byte aligned); bnd = M - s; my / mx: the window is in the last
+// row / column of the grid (shift > 0).  On return o[j] holds the normalised
+// O for the lane's query and d = 8*(l/16) + e, e = 0..7.
+template <typename QT, typename VT, int M, int QTL, bool MASKED>
+__device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int (&tile)[QTL],
+                                           const QT* ks, const VT* vs, const float* rt4,
+                                           const float* ninf, int lane, int bnd, bool my, bool mx,
+                                           float (&o)[QTL][8]) {
+  typedef __attribute__((address_space(3))) const vec8<QT>* lds_q8;
+  typedef __attribute__((address_space(3))) const f32x4* lds_f4;
+  constexpr int N = M * M;
+  constexpr int R = 2 * M - 1;
+  constexpr int LDK = kAttnLD;
+  constexpr int TPC = M / 2;  // 16-query tiles per chunk
+  constexpr int BPC = M / 4;  // 32-key blocks per chunk
+  constexpr int TS = table_stride<M>();
+  const int g4 = lane >> 4, i16 = lane & 15;
+  const float NEG_INF = -__builtin_inff();
+  // Lazy-rescale headroom (base 2): P may reach 2^kGrow before the reference
+  // moves.  bfloat16 P has the float exponent range; float16 P tops out at
+  // 65504, so it keeps a margin of 8.
+  constexpr float kGrow = __is_same(VT, h16) ? 8.0f : 64.0f;
+
+  int qy[QTL], qx[QTL];
+  lds_f4 tb[QTL];
+  f32x4 o0[QTL], o1[QTL], ls[QTL];
+  float m[QTL], mt[QTL];  // reference max and reference + kGrow
+#pragma unroll
+  for (int j = 0; j < QTL; ++j) {
+    const int T = tile[j];
+    const int cq = T / TPC, rp = T - cq * TPC;
+    qy[j] = 2 * rp + (i16 >> 3);
+    qx[j] = 8 * cq + (i16 & 7);
+    // Table row of (qy, key row 4b + g4) is qy - 4b - g4 + M - 1; reversed
+    // column of key column 8c is 8c - qx + M - 1.  a0 is the index at b = BPC-1,
+    // c = 0 (the smallest), so every block adds a non-negative multiple of 4.
+    // Copy (a0 % 4) of the table is shifted so that the lane's 8 floats start
+    // on a 16-byte boundary.
+    const int a0 = (qy[j] - 4 * (BPC - 1) - g4 + M - 1) * R + (M - 1 - qx[j]);
+    tb[j] = (lds_f4)(rt4 + (a0 & 3) * TS + (a0 & ~3));
+    o0[j] = o1[j] = ls[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[j] = -1e30f;
+    mt[j] = -1e30f;
+  }
+  vec8<VT> ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = from_f32<VT>(1.0f);
+  // Per-lane LDS bases: K rows of the block permutation, V for the
+  // transposing reads, the bias.  Opaque, so that every per-block address is
+  // this base plus an immediate (the static LDS offsets of the arrays are not
+  // folded into the immediates, which would overflow their 16 bits), and so
+  // that the ones operand stays in vector registers.
+  lds_q8 kl = (lds_q8)&ks[(8 * (i16 >> 2) + (i16 & 3)) * LDK + g4 * 8];
+  lds_v4s vl = (lds_v4s)&vs[(8 * g4 + (i16 >> 2)) * LDK + 8 * (i16 & 3)];
+  asm volatile("" : "+v"(kl), "+v"(vl), "+v"(ones));
+#pragma unroll
+  for (int j = 0; j < QTL; ++j) asm volatile("" : "+v"(tb[j]));
+  lds_f4 ninf4 = (lds_f4)ninf;
+
+  // Key blocks of 32: block kbi is chunk kbi / BPC, rows 4b .. 4b+3 with
+  // b = kbi % BPC.  Fully unrolled, with the LDS operands of the next block
+  // (K and V fragments, the tiles' biases) loaded while this one is computed.
+  constexpr int NB = N / 32;
+  struct Ops {
+    vec8<QT> k0, k1;
+    vec8<VT> v0, v1;
+    f32x4 b0[QTL], b1[QTL];
+    bool act[QTL];       // tile has an allowed key in this block (masked windows)
+    unsigned bits[QTL];  // allowed keys of the lane's group (masked windows)
+  };
+  auto load = [&](int kbi, Ops& op) {
+    const int ck = kbi / BPC, b = kbi - ck * BPC;
+    const int kb = 32 * kbi;
+    op.k0 = kl[kb * LDK / 8];
+    op.k1 = kl[(kb + 4) * LDK / 8];
+    op.v0 = vt_frag<VT>(vl, kb, 0);
+    op.v1 = vt_frag<VT>(vl, kb, 1);
+    const int boff = 8 * ck + 4 * R * (BPC - 1 - b);
+#pragma unroll
+    for (int j = 0; j < QTL; ++j) {
+      lds_f4 bp = tb[j] + boff / 4;
+      op.act[j] = true;
+      op.bits[j] = 0xffu;
+      if constexpr (MASKED) {
+        // Allowed key columns of this chunk for the lane's query, and rows.
+        const int left = min(max(bnd - 8 * ck, 0), 8);
+        const unsigned lm = (1u << left) - 1u;
+        const unsigned xb = !mx ? 0xffu : (qx[j] < bnd ? lm : (~lm & 0xffu));
+        const int ky = 4 * b + g4;
+        const bool yok = !my || ((ky < bnd) == (qy[j] < bnd));
+        op.bits[j] = yok ? xb : 0u;
+        op.act[j] = __any(op.bits[j] != 0u);  // else the tile is masked in this block
+        if (op.bits[j] == 0u) bp = ninf4;
+      }
+      op.b0[j] = bp[0];
+      op.b1[j] = bp[1];
+    }
+  };
+
+  Ops cur;
+  load(0, cur);
+#pragma unroll
+  for (int kbi = 0; kbi < NB; ++kbi) {
+    Ops nxt;
+    if (kbi + 1 < NB) load(kbi + 1, nxt);
+    const int ck = kbi / BPC;
+    bool straddle = false;
+    if constexpr (MASKED) {
+      const int left = min(max(bnd - 8 * ck, 0), 8);
+      straddle = mx && left > 0 && left < 8;
+    }
+    // Phase 1, every tile: S^T = K Q^T on top of the bias, block max.
+    f32x4 s0[QTL], s1[QTL];
+    float bm[QTL];
+#pragma unroll
+    for (int j = 0; j < QTL; ++j) {
+      s0[j] = cur.b0[j];
+      s1[j] = cur.b1[j];
+      if constexpr (MASKED) {
+        if (straddle) {
+          const unsigned bits = cur.bits[j];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (!((bits >> r) & 1u)) s0[j][r] = NEG_INF;
+            if (!((bits >> (4 + r)) & 1u)) s1[j][r] = NEG_INF;
+          }
+        }
+        if (!cur.act[j]) {
+          bm[j] = NEG_INF;
+          continue;
+        }
+      }
+      s0[j] = mma_16x16x32(cur.k0, qf[j], s0[j]);
+      s1[j] = mma_16x16x32(cur.k1, qf[j], s1[j]);
+      bm[j] = fmaxf(fmaxf(fmaxf(s0[j][0], s0[j][1]), fmaxf(s0[j][2], s0[j][3])),
+                    fmaxf(fmaxf(s1[j][0], s1[j][1]), fmaxf(s1[j][2], s1[j][3])));
+    }
+    // Phase 2, rare: some lane of some tile saw a logit more than kGrow above
+    // its reference; move every tile's reference to its row max.
+    uint64_t grow = 0;
+#pragma unroll
+    for (int j = 0; j < QTL; ++j) grow |= __builtin_amdgcn_ballot_w64(bm[j] > mt[j]);
+    if (grow) {
+#pragma unroll
+      for (int j = 0; j < QTL; ++j) {
+        const float rm = xor32_max(xor16_max(bm[j]));
+        const float mn = fmaxf(m[j], rm);
+        const float alpha = fast_exp2(m[j] - mn);
+        o0[j] *= alpha;
+        o1[j] *= alpha;
+        ls[j] *= alpha;
+        m[j] = mn;
+        mt[j] = mn + kGrow;
+      }
+    }
+    // Phase 3, every tile: P = exp2(S - m), O^T += V^T P^T, row sums.
+#pragma unroll
+    for (int j = 0; j < QTL; ++j) {
+      if constexpr (MASKED) {
+        if (!cur.act[j]) continue;
+      }
+      vec8<VT> pf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pf[r] = from_f32<VT>(fast_exp2(s0[j][r] - m[j]));
+        pf[4 + r] = from_f32<VT>(fast_exp2(s1[j][r] - m[j]));
+      }
+      o0[j] = mma_16x16x32(cur.v0, pf, o0[j]);
+      o1[j] = mma_16x16x32(cur.v1, pf, o1[j]);
+      ls[j] = mma_16x16x32(ones, pf, ls[j]);
+    }
+    if (kbi + 1 < NB) cur = nxt;
+  }
+
+  // Fragment pair t row 4*g4 + r is head dim 8*g4 + 4t + r.
+#pragma unroll
+  for (int j = 0; j < QTL; ++j) {
+    const float inv = __builtin_amdgcn_rcpf(ls[j][0]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      o[j][r] = o0[j][r] * inv;
+      o[j][4 + r] = o1[j][r] * inv;
+    }
+  }
+}
+
+}  // namespace swin

@@ -58,6 +58,10 @@ hipError_t launch_tiled_attn(const FwdParams& p, hipStream_t st);
 bool tiled_gemm_supported(int C, int io);
 hipError_t launch_qkv_tiled(const FwdParams& p, hipStream_t st);
 hipError_t launch_proj_tiled(const FwdParams& p, hipStream_t st);
+// Single-kernel forward for window side 16 with C = 32 * heads, heads <= 4,
+// 16-bit I/O (needs chunked slots).
+bool fused_w16_supported(int M, int C, int heads, int io);
+hipError_t launch_fused_w16(const FwdParams& p, hipStream_t st);
 // Single-kernel forward for N <= 64 and C = 32 * heads with heads <= 4.
 hipError_t launch_fused_window(const FwdParams& p, hipStream_t st);
 

@@ -54,13 +54,15 @@ def _desc(**kw):
 def test_workspace_size(lib):
     # small windows with <= 4 heads run as one fused kernel: no workspace
     assert swin.workspace_size(_desc()) == 0
-    d = _desc(H=64, W=64, C=128, heads=4, M=16, s=8)
+    # window 16 with <= 4 heads and 16-bit I/O is fused too
+    assert swin.workspace_size(_desc(H=64, W=64, C=128, heads=4, M=16, s=8)) == 0
+    d = _desc(H=64, W=64, C=160, heads=5, M=16, s=8)
     T = 2 * 64 * 64
-    assert swin.workspace_size(d) >= 4 * T * 128 * 2
+    assert swin.workspace_size(d) >= 4 * T * 160 * 2
     assert swin.workspace_size(_desc(B=0)) == 0
     assert swin.workspace_size(_desc(H=50)) == 0          # invalid -> 0
     # V2 with bf16 keeps q and k in float16: same byte count as bf16
-    assert swin.workspace_size(swin.make_desc(2, 64, 64, 128, 4, 16, 8, "v2", torch.bfloat16)) == \
+    assert swin.workspace_size(swin.make_desc(2, 64, 64, 160, 5, 16, 8, "v2", torch.bfloat16)) == \
         swin.workspace_size(d)
     d32 = swin.make_desc(2, 64, 64, 128, 4, 16, 8, "v1", torch.float32)
     assert swin.workspace_size(d32) >= 4 * T * 128 * 4
@@ -78,7 +80,7 @@ def _fwd(lib, d, x=FAKE, wq=FAKE * 2, wp=FAKE * 3, tab=FAKE * 4, tau=FAKE * 5, y
 
 
 def test_fwd_rejects_before_launch(lib):
-    small = _desc(B=1, H=16, W=16, C=32, heads=1, M=16, s=3)
+    small = _desc(B=1, H=16, W=16, C=160, heads=5, M=16, s=3)  # needs a workspace
     assert _fwd(lib, _desc(H=50)) == SHAPE                   # H % M
     assert _fwd(lib, _desc(s=7)) == SHAPE                    # s >= M
     assert _fwd(lib, _desc(s=-1)) == SHAPE
@@ -129,7 +131,9 @@ def test_kernel_names_and_timed_rejects(lib):
     d = _desc(H=64, W=64, C=128, heads=4, M=16, s=8)
     tiled = ["qkv_tiled_kernel", "tiled_attn_kernel", "proj_tiled_kernel"]
     three = ["qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"]
-    assert swin.kernel_names(d) == ["qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"]
+    assert swin.kernel_names(d) == ["fused_w16_kernel"]
+    assert swin.kernel_names(_desc(H=64, W=64, C=160, heads=5, M=16, s=8)) == [
+        "qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"]
     assert swin.kernel_names(_desc(H=48, W=48, M=24, s=12, C=512, heads=16,
                                    dtype=torch.bfloat16)) == tiled
     assert swin.kernel_names(_desc(H=64, W=64, M=16, s=8, C=128, heads=4,
@@ -140,11 +144,10 @@ def test_kernel_names_and_timed_rejects(lib):
     assert swin.kernel_names(_desc(H=48, W=48, M=12, s=6, C=128, heads=4)) == three
     assert swin.kernel_names(_desc(H=48, W=48, M=12, s=6, C=256, heads=8)) == [
         "qkv_tiled_kernel", "window_attn_kernel", "proj_tiled_kernel"]
-    assert swin.kernel_names(_desc(H=48, W=48, M=16, s=6, C=96, heads=3)) == [
-        "qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"]
+    assert swin.kernel_names(_desc(H=48, W=48, M=16, s=6, C=96, heads=3)) == ["fused_w16_kernel"]
     assert lib.swin_wmsa_kernel_count(ctypes.byref(_desc(H=50))) == 0
     assert lib.swin_wmsa_kernel_name(ctypes.byref(d), 3) is None
-    small = _desc(B=1, H=16, W=16, C=32, heads=1, M=16, s=3)
+    small = _desc(B=1, H=16, W=16, C=160, heads=5, M=16, s=3)  # needs a workspace
     ws = lib.swin_wmsa_workspace_size(ctypes.byref(small))
     ev = (ctypes.c_void_p * 4)(FAKE * 64, FAKE * 65, FAKE * 66, FAKE * 67)
     args = (ctypes.byref(small), FAKE, FAKE * 2, None, FAKE * 3, None, FAKE * 4, None, FAKE * 8,

@@ -99,6 +99,8 @@ SMALL = [
     (2, 48, 24, 96, 3, 24, 7, "fp16", "v2", 0.1),    # split 17: inside chunk 2
     (1, 16, 16, 32, 1, 16, 8, "bf16", "v1", 0.3),    # window = image, shifted
     (1, 24, 48, 160, 5, 8, 0, "bf16", "v2", 0.1),    # no shift
+    (1, 32, 32, 160, 5, 16, 8, "bf16", "v2", 0.1),   # window 16, 5 heads: three kernels
+    (2, 32, 48, 96, 3, 16, 11, "fp16", "v1", 0.1),   # fused window 16: split 5 in chunk 0
 ]
 
 
