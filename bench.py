@@ -62,6 +62,7 @@ def stage_work(case):
     return {
         "fused_window_kernel": ((8 * C * C + 4 * N * C) * T, T * 2 * C * e + 4 * C * C * e + tab),
         "fused_w16_kernel": ((8 * C * C + 4 * N * C) * T, T * 2 * C * e + 4 * C * C * e + tab),
+        "fused_w8_kernel": ((8 * C * C + 4 * N * C) * T, T * 2 * C * e + 4 * C * C * e + tab),
         "qkv_gemm_kernel": (6 * C * C * T, T * (C * e + 2 * C * eqk + C * e) + 3 * C * C * e),
         "qkv_tiled_kernel": (6 * C * C * T, T * (C * e + 2 * C * eqk + C * e) + 3 * C * C * e),
         "proj_tiled_kernel": (2 * C * C * T, T * 2 * C * e + C * C * e),

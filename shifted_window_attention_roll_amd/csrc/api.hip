@@ -59,11 +59,12 @@ int qk_type(const swin_wmsa_desc* d) {
   return d->dtype == SWIN_F16 ? kF16 : kBF16;
 }
 
-// Kernel plan: one fused kernel for small windows with few heads, and for
-// window side 16 with few heads and 16-bit I/O; else the QKV GEMM -> window
+// Kernel plan: one fused kernel for small windows with few heads (a dedicated
+// one for window sides 7 and 8 with 16-bit I/O), and for window side 16 with
+// few heads and 16-bit I/O; else the QKV GEMM -> window
 // attention -> projection GEMM sequence through the workspace, with the tiled
 // attention (chunked slots) for 16-bit I/O and window sides 8, 16, 24.
-enum Plan { kPlanFusedSmall = 0, kPlanThree = 1, kPlanTiled = 2, kPlanFusedW16 = 3 };
+enum Plan { kPlanFusedSmall = 0, kPlanThree = 1, kPlanTiled = 2, kPlanFusedW16 = 3, kPlanFusedW8 = 4 };
 
 int io_type(const swin_wmsa_desc* d) {
   return d->dtype == SWIN_F32 ? kF32 : d->dtype == SWIN_F16 ? kF16 : kBF16;
@@ -71,6 +72,7 @@ int io_type(const swin_wmsa_desc* d) {
 
 Plan choose_plan(const swin_wmsa_desc* d) {
   const int heads = d->heads;
+  if (fused_w8_supported(d->M, d->C, heads, io_type(d))) return kPlanFusedW8;
   if (d->M * d->M <= 64 && heads <= 4 && d->C == kHeadDim * heads) return kPlanFusedSmall;
   if (fused_w16_supported(d->M, d->C, heads, io_type(d))) return kPlanFusedW16;
   if (tiled_attn_supported(d->M, io_type(d))) return kPlanTiled;
@@ -88,7 +90,8 @@ struct WsLayout {
 
 WsLayout ws_layout(const swin_wmsa_desc* d) {
   const Plan plan = choose_plan(d);
-  if (plan == kPlanFusedSmall || plan == kPlanFusedW16) return WsLayout{0, 0, 0, 0, 0};
+  if (plan == kPlanFusedSmall || plan == kPlanFusedW16 || plan == kPlanFusedW8)
+    return WsLayout{0, 0, 0, 0, 0};
   const size_t tokens = (size_t)d->B * d->H * d->W;
   const size_t e = elem_bytes(d->dtype);
   const size_t eq = qk_type(d) == kF32 ? 4 : 2;
@@ -182,12 +185,13 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
   return ws_layout(d).total;
 }
 
-static const int kPlanCount[4] = {1, 3, 3, 1};
+static const int kPlanCount[5] = {1, 3, 3, 1, 1};
 
 static const char* stage_name(const swin_wmsa_desc* d, int i) {
   const Plan plan = choose_plan(d);
   if (plan == kPlanFusedSmall) return "fused_window_kernel";
   if (plan == kPlanFusedW16) return "fused_w16_kernel";
+  if (plan == kPlanFusedW8) return "fused_w8_kernel";
   const bool tg = use_tiled_gemm(d);
   if (i == 0) return tg ? "qkv_tiled_kernel" : "qkv_gemm_kernel";
   if (i == 1) return plan == kPlanTiled ? "tiled_attn_kernel" : "window_attn_kernel";
@@ -266,9 +270,11 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
   };
   hipError_t err = mark(0);
-  if (plan == kPlanFusedSmall || plan == kPlanFusedW16) {
+  if (plan == kPlanFusedSmall || plan == kPlanFusedW16 || plan == kPlanFusedW8) {
     if (err == hipSuccess)
-      err = plan == kPlanFusedSmall ? launch_fused_window(p, hs) : launch_fused_w16(p, hs);
+      err = plan == kPlanFusedSmall ? launch_fused_window(p, hs)
+            : plan == kPlanFusedW16 ? launch_fused_w16(p, hs)
+                                    : launch_fused_w8(p, hs);
     if (err == hipSuccess) err = mark(1);
     return from_hip(err);
   }

@@ -101,6 +101,13 @@ SMALL = [
     (1, 24, 48, 160, 5, 8, 0, "bf16", "v2", 0.1),    # no shift
     (1, 32, 32, 160, 5, 16, 8, "bf16", "v2", 0.1),   # window 16, 5 heads: three kernels
     (2, 32, 48, 96, 3, 16, 11, "fp16", "v1", 0.1),   # fused window 16: split 5 in chunk 0
+    # fused window 7 / 8 (8 x 8 slot grid): heads 1 - 4, both modes, splits 1 .. 7
+    (1, 14, 14, 32, 1, 7, 3, "fp16", "v2", 0.1),
+    (2, 16, 16, 128, 4, 8, 4, "bf16", "v2", 0.1),
+    (1, 21, 14, 96, 3, 7, 5, "bf16", "v2", 0.1),     # H != W, split 2
+    (2, 24, 16, 64, 2, 8, 1, "fp16", "v1", 0.1),     # split 7
+    (1, 7, 7, 96, 3, 7, 3, "fp16", "v1", 0.3),       # window = image, shifted
+    (3, 16, 24, 128, 4, 8, 0, "fp16", "v2", 0.1),    # no shift
 ]
 
 
@@ -125,9 +132,14 @@ def test_wmsa_empty_batch(gpu):
     assert y.shape == x.shape
 
 
-def test_wmsa_deterministic_and_every_output_written(gpu):
-    _say("determinism")
-    case = workloads.make_case(4, 32, 32, 128, 4, 16, (8,), "bf16", "v2", seed=5, tau="uniform")
+@pytest.mark.parametrize("B,H,W,C,heads,M,s,dtype,mode", [
+    (4, 32, 32, 128, 4, 16, 8, "bf16", "v2"),
+    # 1280 windows: more than the persistent grid of the window-7 kernel holds at once
+    (20, 56, 56, 96, 3, 7, 3, "fp16", "v1"),
+])
+def test_wmsa_deterministic_and_every_output_written(gpu, B, H, W, C, heads, M, s, dtype, mode):
+    _say(f"determinism B={B} H={H} W={W} C={C} M={M} {dtype} {mode}")
+    case = workloads.make_case(B, H, W, C, heads, M, (s,), dtype, mode, seed=5, tau="uniform")
     blk = case.blocks[0]
     x = case.x.cuda()
     out = torch.full_like(x, float("nan"))
