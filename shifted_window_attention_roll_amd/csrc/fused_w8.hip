@@ -25,9 +25,11 @@
 //   -- workgroup barrier: every head's O is in LDS --
 //   3. output channels 32h .. 32h+31 of the projection for the 64 slots, plus
 //      bias, stored straight to the un-shifted token rows (16 bytes a lane).
-// The next window's token rows and first weight fragments are loaded while
-// the projection runs; a second barrier (after the next window's q) keeps its
-// K stores behind every wave's projection reads.
+// With up to 3 heads a wave keeps its weights (its head's q, k, v rows and its
+// 32 projection rows) in registers for the whole kernel and loads the next
+// window's token rows right after its attention; with 4 heads it reloads
+// weights and rows per window.  A second barrier (after the next window's q)
+// keeps the K stores behind every wave's projection reads.
 #include "attn_core.hpp"
 #include "launch.hpp"
 
@@ -48,7 +50,7 @@ template <typename QT, typename T, int MV, bool MASKED>
 __device__ __forceinline__ void w8_attend(const vec8<QT> (&qf)[4], const vec8<QT> (&kf)[2][2],
                                           const vec8<T> (&vf)[2][2], lds_f tb0,
                                           lds_f tb1, int qy0, int qx, int g4, int bnd,
-                                          bool my, bool mx, vec8<T> (&of)[4]) {
+                                          bool my, bool mx, T* os) {
   const float NEG_INF = -__builtin_inff();
   vec8<T> ones;
 #pragma unroll
@@ -111,18 +113,30 @@ __device__ __forceinline__ void w8_attend(const vec8<QT> (&qf)[4], const vec8<QT
       l = mma_16x16x32(ones, pf, l);
     }
     const float inv = __builtin_amdgcn_rcpf(l[0]);
+    vec8<T> of;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      of[j][r] = from_f32<T>(o0[r] * inv);
-      of[j][4 + r] = from_f32<T>(o1[r] * inv);
+      of[r] = from_f32<T>(o0[r] * inv);
+      of[4 + r] = from_f32<T>(o1[r] * inv);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // O of the lane's query, dims 8g .. 8g+7: into the wave's K rows, whose
+    // fragments are all in registers already.
+    store8(os + 16 * j * kAttnLD, of);
   }
 }
 
+// Waves per SIMD the kernel is compiled for: with up to 3 heads the wave keeps
+// all of its weights in registers across windows (2 waves per SIMD at 2 and 3
+// heads); with 4 it reloads them per window.
+template <int HEADS>
+constexpr bool w8_resident() { return HEADS <= 3; }
+template <int HEADS>
+constexpr int w8_waves_per_simd() { return HEADS == 2 || HEADS == 3 ? 2 : 3; }
+
 template <typename T, typename QT, int HEADS, int MV, bool V2>
-__global__ __launch_bounds__(64 * HEADS) __attribute__((amdgpu_waves_per_eu(3))) void fused_w8_kernel(FwdParams p,
-                                                                          int n_windows) {
+__global__ __launch_bounds__(64 * HEADS) __attribute__((amdgpu_waves_per_eu(w8_waves_per_simd<HEADS>())))
+void fused_w8_kernel(FwdParams p, int n_windows) {
+  constexpr bool RES = w8_resident<HEADS>();
   constexpr int C = 32 * HEADS, D = 32, LDK = kAttnLD;
   constexpr int NT = 64 * HEADS;
   static_assert(MV == 7 || MV == 8, "window side");
@@ -213,8 +227,24 @@ __global__ __launch_bounds__(64 * HEADS) __attribute__((amdgpu_waves_per_eu(3)))
         xf[j][kk] = gload8(x + (int64_t)row[j] * C + 32 * kk + 8 * g4);
   };
 
+  auto wp_frags = [&](vec8<T> (&f)[2][HEADS]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kk = 0; kk < HEADS; ++kk)
+        f[t][kk] = gload8(wp + (uint32_t)((h * D + prow + 4 * t) * C + 32 * kk + 8 * g4));
+  };
+
   int row[4];
-  vec8<T> wf[2][HEADS];
+  // Resident weights: q, k, v rows of head h and projection rows 32h .. 32h+31.
+  vec8<T> wres[3][2][HEADS], wpres[2][HEADS];
+  if constexpr (RES) {
+#pragma unroll
+    for (int pt = 0; pt < 3; ++pt) wq_frags(pt, wres[pt]);
+    wp_frags(wpres);
+    locate(w, row);
+    fetch_x(row);
+  }
   __syncthreads();  // tables and biases
 
   const float eps2 = p.eps * p.eps;
@@ -223,21 +253,31 @@ __global__ __launch_bounds__(64 * HEADS) __attribute__((amdgpu_waves_per_eu(3)))
   const int bnd = MV - g.s;
 
   for (; w < n_windows; w += gridDim.x) {
-    // With 3 or 4 heads the weights do not fit in registers across windows:
-    // keep their loads inside the loop.
-    if constexpr (HEADS > 2) asm volatile("" : "+s"(wq), "+s"(wp));
     const int wl = w - (int)fdiv((uint32_t)w, g.dnW) * g.nW;
     const int wy = (int)fdiv((uint32_t)wl, g.dnWx);
     const bool my = g.s > 0 && wy == g.H / MV - 1;
     const bool mx = g.s > 0 && wl - wy * g.nWx == g.nWx - 1;
-    locate(w, row);
-    fetch_x(row);
+    if constexpr (!RES) {
+      // The weights do not fit in registers across windows: keep their loads
+      // inside the loop.
+      asm volatile("" : "+s"(wq), "+s"(wp));
+      locate(w, row);
+      fetch_x(row);
+    }
 
     // ---- 1. q, k, v of head h -----------------------------------------------
     vec8<QT> qf[4];
 #pragma unroll
     for (int pt = 0; pt < 3; ++pt) {
-      wq_frags(pt, wf);
+      vec8<T> wf[2][HEADS];
+      if constexpr (RES) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int kk = 0; kk < HEADS; ++kk) wf[t][kk] = wres[pt][t][kk];
+      } else {
+        wq_frags(pt, wf);
+      }
       const f32x4 b0 = *reinterpret_cast<const f32x4*>(&lb[pt * C + h * D + 8 * g4]);
       const f32x4 b1 = *reinterpret_cast<const f32x4*>(&lb[pt * C + h * D + 8 * g4 + 4]);
       f32x4 acc[2][4];
@@ -287,7 +327,6 @@ __global__ __launch_bounds__(64 * HEADS) __attribute__((amdgpu_waves_per_eu(3)))
       // Every wave's projection has read the previous window's O (which lives
       // in the K rows) before any K row is overwritten.
       if (pt == 0) __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
     }
     // The wave reads back only rows it wrote itself (LDS is in order per wave).
     asm volatile("" ::: "memory");
@@ -302,22 +341,34 @@ __global__ __launch_bounds__(64 * HEADS) __attribute__((amdgpu_waves_per_eu(3)))
         kf[b][t] = kl[(32 * b + 4 * t) * LDK / 8];
         vf[b][t] = vt_frag<T>(vl, 32 * b, t);
       }
-    vec8<T> of[4];
+    T* os = reinterpret_cast<T*>(ks[h]) + i16 * LDK + 8 * g4;
     if (my || mx)
-      w8_attend<QT, T, MV, true>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, my, mx, of);
+      w8_attend<QT, T, MV, true>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, my, mx, os);
     else
-      w8_attend<QT, T, MV, false>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, false, false, of);
-    // Projection weights of output channels 32h .. 32h+31, in flight across
-    // the barrier.
+      w8_attend<QT, T, MV, false>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, false, false, os);
+    // The next window's token rows, in flight across the barrier and the
+    // projection.
+    int cur[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cur[j] = row[j];
+    if constexpr (RES) {
+      const int nxt = w + gridDim.x;
+      if (nxt < n_windows) {
+        locate(nxt, row);
+        fetch_x(row);
+      }
+    }
+    // Projection weights of output channels 32h .. 32h+31 (reloaded: in flight
+    // across the barrier).
     vec8<T> wpf[2][HEADS];
+    if constexpr (RES) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int kk = 0; kk < HEADS; ++kk)
-        wpf[t][kk] = gload8(wp + (uint32_t)((h * D + prow + 4 * t) * C + 32 * kk + 8 * g4));
-    T* os = reinterpret_cast<T*>(ks[h]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) store8(&os[(16 * j + i16) * LDK + 8 * g4], of[j]);
+        for (int kk = 0; kk < HEADS; ++kk) wpf[t][kk] = wpres[t][kk];
+    } else {
+      wp_frags(wpf);
+    }
     __syncthreads();  // every head's O in LDS
 
     // ---- 3. projection, output channels 32h .. 32h+31 ------------------------
@@ -346,7 +397,7 @@ __global__ __launch_bounds__(64 * HEADS) __attribute__((amdgpu_waves_per_eu(3)))
       vec8<T> v;
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = from_f32<T>(ya[e >> 2][j][e & 3]);
-      gstore16(y + (int64_t)row[j] * C + h * D + 8 * g4, __builtin_bit_cast(uint4, v));
+      gstore16(y + (int64_t)cur[j] * C + h * D + 8 * g4, __builtin_bit_cast(uint4, v));
     }
   }
 }
@@ -359,7 +410,7 @@ hipError_t w8_heads(const FwdParams& p, int cus, hipStream_t st) {
   // most 12 waves.
   const int lds = heads * (2 * 64 * kAttnLD * 2 + kTab * 4) + 16 * 32 * heads;
   int per_cu = (160 * 1024) / lds;
-  const int wave_cap = 12 / heads;
+  const int wave_cap = 4 * (heads == 2 || heads == 3 ? 2 : 3) / heads;  // w8_waves_per_simd
   per_cu = per_cu > wave_cap ? wave_cap : (per_cu < 1 ? 1 : per_cu);
   const int grid = n < cus * per_cu ? n : cus * per_cu;
   const dim3 block(64 * heads);

@@ -139,6 +139,8 @@ def test_kernel_names_and_timed_rejects(lib):
     assert swin.kernel_names(_desc(H=64, W=64, M=16, s=8, C=128, heads=4,
                                    dtype=torch.float32)) == three
     assert swin.kernel_names(_desc()) == ["fused_w8_kernel"]
+    assert swin.kernel_names(_desc(H=48, W=48, M=8, s=4, C=64, heads=2,
+                                   dtype=torch.bfloat16, mode="v2")) == ["fused_w8_kernel"]
     assert swin.kernel_names(_desc(H=48, W=48, M=8, s=4, C=128, heads=4,
                                    dtype=torch.bfloat16, mode="v2")) == ["fused_w8_kernel"]
     assert swin.kernel_names(_desc(dtype=torch.float32)) == ["fused_window_kernel"]

@@ -103,7 +103,9 @@ SMALL = [
     (2, 32, 48, 96, 3, 16, 11, "fp16", "v1", 0.1),   # fused window 16: split 5 in chunk 0
     # fused window 7 / 8 (8 x 8 slot grid): heads 1 - 4, both modes, splits 1 .. 7
     (1, 14, 14, 32, 1, 7, 3, "fp16", "v2", 0.1),
-    (2, 16, 16, 128, 4, 8, 4, "bf16", "v2", 0.1),
+    (2, 16, 16, 128, 4, 8, 4, "bf16", "v2", 0.1),     # 4 heads: weights reloaded per window
+    (2, 16, 16, 64, 2, 8, 4, "bf16", "v2", 0.1),
+    (3, 14, 21, 96, 3, 7, 3, "bf16", "v1", 0.1),     # 18 windows
     (1, 21, 14, 96, 3, 7, 5, "bf16", "v2", 0.1),     # H != W, split 2
     (2, 24, 16, 64, 2, 8, 1, "fp16", "v1", 0.1),     # split 7
     (1, 7, 7, 96, 3, 7, 3, "fp16", "v1", 0.3),       # window = image, shifted
