@@ -178,9 +178,26 @@ class Runner:
         return {k: v / (steps * nb) for k, v in tot.items()}
 
 
-def source_digest():
+# Source file of each kernel; its digest also covers the shared headers and the
+# host-side launch code, so traffic counters taken on a kernel stay valid while
+# only other kernels change.
+KERNEL_SOURCE = {
+    "fused_window_kernel": "fused_window.hip", "fused_w8_kernel": "fused_w8.hip",
+    "fused_w16_kernel": "fused_w16.hip", "tiled_attn_kernel": "tiled_attn.hip",
+    "window_attn_kernel": "window_attn.hip", "qkv_tiled_kernel": "gemm_tiled.hip",
+    "proj_tiled_kernel": "gemm_tiled.hip", "qkv_gemm_kernel": "gemm.hip",
+    "proj_gemm_kernel": "gemm.hip",
+}
+
+
+def source_digest(kernel=None):
+    csrc = os.path.join(ROOT, "shifted_window_attention_roll_amd", "csrc")
+    paths = sorted(glob.glob(os.path.join(csrc, "*")))
+    if kernel in KERNEL_SOURCE:
+        own = KERNEL_SOURCE[kernel]
+        paths = [p for p in paths if p.endswith(".hpp") or os.path.basename(p) in (own, "api.hip")]
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "shifted_window_attention_roll_amd", "csrc", "*"))):
+    for p in paths:
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())
@@ -196,7 +213,7 @@ def measured_traffic(kernel, workload):
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get("entries", {}).get(f"{workload}:{kernel}")
-    if not ent or ent.get("source_digest") != source_digest():
+    if not ent or ent.get("source_digest") != source_digest(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -369,7 +386,7 @@ def traffic_summarize(name, fetch_dir, write_dir, command):
         rec["entries"][f"{name}:{k}"] = {
             "fetch_kib": fk[k][0], "write_kib": wk[k][0], "fetch_scale": fscale,
             "write_scale": wscale, "bytes_per_launch": b, "algorithmic_bytes": alg,
-            "source_digest": source_digest(), "command": command}
+            "source_digest": source_digest(k), "command": command}
         lines.append(f"| {k} | {fk[k][1]} | {fk[k][0]:.1f} | {wk[k][0]:.1f} | {b:.4g} | "
                      f"{alg:.4g} | {b / alg:.3f} |")
     with open(path, "w") as f:
