@@ -56,6 +56,10 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
   __shared__ __attribute__((aligned(16))) T vs[N * LDK];
   __shared__ __attribute__((aligned(16))) float rt4[4 * TS];
   __shared__ __attribute__((aligned(16))) float ninf[8];
+  // The head's projection columns Wp[:, h*32 .. +31] in fragment order:
+  // fragment c (output channel tile) is 64 lanes x 16 bytes, lane l holding
+  // row 32(c/2) + 8(l%16 / 4) + 4(c%2) + l%4, columns h*32 + 8(l/16) .. +7.
+  __shared__ __attribute__((aligned(16))) T wps[C / 16 * 512];
   __shared__ float bqs[3 * C], bps[C];  // linear biases
 
   const Geom& g = p.g;
@@ -69,13 +73,7 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
   const T* bq = static_cast<const T*>(p.b_qkv);
   const T* bp = static_cast<const T*>(p.b_proj);
 
-  // Window rows, gathered through the shift + partition map.
   constexpr int XCH = C / 8;  // 16-byte chunks per row
-  for (int i = tid; i < N * XCH; i += NT) {
-    const int r = i / XCH, c = i - r * XCH;
-    *reinterpret_cast<uint4*>(&xs[r * LDX + 8 * c]) =
-        gload16(x + src_token(g, w * N + r) * C + 8 * c);
-  }
   if (tid < 8) ninf[tid] = -__builtin_inff();
   for (int i = tid; i < 4 * C; i += NT) {
     if (i < 3 * C)
@@ -104,12 +102,14 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
   // consecutive channels.
   const int prow0 = 8 * (i16 >> 2) + (i16 & 3);
 
-  // A head's q, k, v weight rows and bias-table entries go through registers
-  // (loaded during the previous head, stored to LDS at the head's start).
+  // A head's q, k, v weight rows, projection columns and bias-table entries go
+  // through registers (loaded during the previous head, stored to LDS at the
+  // head's start).
   constexpr int WPT = (96 * XCH + NT - 1) / NT;   // 16-byte weight chunks per thread
+  constexpr int PPT = (CT * 64 + NT - 1) / NT;    // 16-byte projection chunks per thread
   constexpr int TPT = (4 * TS + NT - 1) / NT;     // table floats per thread
   constexpr int R = 2 * M - 1;
-  uint4 wreg[WPT];
+  uint4 wreg[WPT], preg[PPT];
   float treg[TPT];
   auto fetch_head = [&](int hh) {
 #pragma unroll
@@ -118,6 +118,15 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
       if (i < 96 * XCH) {
         const int r = i / XCH, c = i - r * XCH;
         wreg[k] = gload16(wq + (int64_t)((r >> 5) * C + hh * D + (r & 31)) * C + 8 * c);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int q = tid + k * NT;
+      if (q < CT * 64) {
+        const int c = q >> 6, l = q & 63;
+        const int row = 32 * (c >> 1) + 8 * ((l & 15) >> 2) + (l & 3) + 4 * (c & 1);
+        preg[k] = gload16(wp + (int64_t)row * C + hh * D + 8 * (l >> 4));
       }
     }
 #pragma unroll
@@ -139,12 +148,23 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
       }
     }
 #pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int q = tid + k * NT;
+      if (q < CT * 64) *reinterpret_cast<uint4*>(&wps[q * 8]) = preg[k];
+    }
+#pragma unroll
     for (int k = 0; k < TPT; ++k) {
       const int i = tid + k * NT;
       if (i < 4 * TS) rt4[i] = treg[k];
     }
   };
-  fetch_head(0);
+  fetch_head(0);  // in flight together with the window rows
+  // Window rows, gathered through the shift + partition map.
+  for (int i = tid; i < N * XCH; i += NT) {
+    const int r = i / XCH, c = i - r * XCH;
+    *reinterpret_cast<uint4*>(&xs[r * LDX + 8 * c]) =
+        gload16(x + src_token(g, w * N + r) * C + 8 * c);
+  }
 
   for (int h = 0; h < HEADS; ++h) {
     if (h > 0) __syncthreads();  // every wave is done with the previous head's table
@@ -230,15 +250,14 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
       attn_tiles<QT, T, M, QTL, false>(qf, tile, ks, vs, rt4, ninf, lane, M - g.s, false, false,
                                        o);
 
-    // 4. Y^T += Wp[:, h*32 .. +31] O_h^T; the Wp rows of each channel-tile pair
-    //    are interleaved like the QKV weight rows.
+    // 4. Y^T += Wp[:, h*32 .. +31] O_h^T (fragments from LDS); the Wp rows of
+    //    each channel-tile pair are interleaved like the QKV weight rows.
     vec8<T> of[QTL];
 #pragma unroll
     for (int j = 0; j < QTL; ++j) of[j] = to_vec8<T>(o[j], 1.0f);
 #pragma unroll
     for (int c = 0; c < CT; ++c) {
-      const vec8<T> wpf =
-          gload8(wp + (int64_t)(32 * (c >> 1) + prow0 + 4 * (c & 1)) * C + h * D + 8 * g4);
+      const vec8<T> wpf = load8(&wps[(c * 64 + lane) * 8]);
 #pragma unroll
       for (int j = 0; j < QTL; ++j) yacc[j][c] = mma_16x16x32(wpf, of[j], yacc[j][c]);
     }
