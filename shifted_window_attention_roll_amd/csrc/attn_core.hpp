@@ -47,7 +47,41 @@ namespace swin {
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s;
 
-constexpr int kAttnLD = 40;  // LDS row pitch (elements) of staged K and V
+constexpr int kAttnLD = 40;  // LDS row pitch (elements) of staged K and V, padded layout
+
+// Second K / V layout (KvLayout::kSwizzled): rows of 32 elements, the 16-byte
+// chunk c of row r stored at chunk c ^ ((r / 8) % 4) -- no padding, and the
+// fragment reads below stay free of bank conflicts.
+enum class KvLayout { kPadded, kSwizzled };
+__device__ __forceinline__ int kv_swz(int r, int c) { return r * 32 + ((c ^ ((r >> 3) & 3)) << 3); }
+
+// Bias-table modes: kTable4 = four shifted copies (fill_bias_copies; two
+// aligned 16-byte reads per lane and block), kTable1 = one copy
+// (fill_bias_table; eight 4-byte reads).
+enum class TableMode { kTable4, kTable1 };
+
+// Floats of the single reversed copy: every lane reads 8 floats from a start
+// index below (2M-1)^2.
+template <int M>
+constexpr int table1_size() { return ((2 * M - 1) * (2 * M - 1) + 8 + 3) / 4 * 4; }
+
+template <int M>
+__device__ __forceinline__ void fill_bias_table(float* rt, const float* table, int heads, int h,
+                                                int tid, int nthreads) {
+  constexpr int R = 2 * M - 1;
+  for (int e = tid; e < table1_size<M>(); e += nthreads) {
+    float v = -__builtin_inff();
+    if (e < R * R) {
+      const int r = e / R, cc = e - r * R;
+      v = table[(int64_t)(r * R + (R - 1 - cc)) * heads + h] * kLog2e;
+    }
+    rt[e] = v;
+  }
+}
+
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
 
 // Floats per copy of the reversed bias table (+ room so that every copy can
 // be read 8 floats past any start index it is used with).
@@ -81,11 +115,11 @@ __device__ __forceinline__ void fill_bias_copies(float* rt4, const float* table,
 // V[kb + 8g + 4h + e][8a + 4t + b]: row i of fragment t is head dim
 // 8a + 4t + b, its k-slice the keys 8g .. 8g+7.
 // vl: this lane's address for kb = 0, t = 0, h = 0.
-template <typename VT>
+template <typename VT, int LD = kAttnLD>
 __device__ __forceinline__ vec8<VT> vt_frag(lds_v4s vl, int kb, int t) {
-  const lds_v4s p0 = vl + (kb * kAttnLD + 4 * t) / 4;
+  const lds_v4s p0 = vl + (kb * LD + 4 * t) / 4;
   const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0 + kAttnLD);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0 + LD);  // 4 rows on
   typedef short v8s __attribute__((ext_vector_type(8)));
   const v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(vec8<VT>, both);
@@ -96,17 +130,24 @@ __device__ __forceinline__ vec8<VT> vt_frag(lds_v4s vl, int kb, int t) {
 // N keys.  ks, vs: K and V as [N][kAttnLD]; rt4: the 4 bias copies; ninf: 8 x
 // -inf (16-byte aligned); bnd = M - s; my / mx: the window is in the last
 // row / column of the grid (shift > 0).  On return o[j] holds the normalised
-// O for the lane's query and d = 8*(l/16) + e, e = 0..7.
-template <typename QT, typename VT, int M, int QTL, bool MASKED>
+// O for the lane's query and d = 8*(l/16) + e, e = 0..7.  LAYOUT / TABLE pick
+// the K, V layout and the bias-table mode; hook(kbi) runs at the start of key
+// block kbi (the caller's work to interleave, e.g. staging the next item).
+template <typename QT, typename VT, int M, int QTL, bool MASKED,
+          KvLayout LAYOUT = KvLayout::kPadded, TableMode TABLE = TableMode::kTable4,
+          class Hook = NoHook>
 __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int (&tile)[QTL],
                                            const QT* ks, const VT* vs, const float* rt4,
                                            const float* ninf, int lane, int bnd, bool my, bool mx,
-                                           float (&o)[QTL][8]) {
+                                           float (&o)[QTL][8], Hook hook = Hook()) {
   typedef __attribute__((address_space(3))) const vec8<QT>* lds_q8;
   typedef __attribute__((address_space(3))) const f32x4* lds_f4;
   constexpr int N = M * M;
   constexpr int R = 2 * M - 1;
-  constexpr int LDK = kAttnLD;
+  constexpr bool SWZ = LAYOUT == KvLayout::kSwizzled;
+  constexpr bool T1 = TABLE == TableMode::kTable1;
+  constexpr int LDK = SWZ ? 32 : kAttnLD;
+  typedef __attribute__((address_space(3))) const float* lds_f;
   constexpr int TPC = M / 2;  // 16-query tiles per chunk
   constexpr int BPC = M / 4;  // 32-key blocks per chunk
   constexpr int TS = table_stride<M>();
@@ -118,7 +159,8 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
   constexpr float kGrow = __is_same(VT, h16) ? 8.0f : 64.0f;
 
   int qy[QTL], qx[QTL];
-  lds_f4 tb[QTL];
+  lds_f4 tb[QTL];   // TABLE == kTable4
+  lds_f tbf[QTL];   // TABLE == kTable1
   f32x4 o0[QTL], o1[QTL], ls[QTL];
   float m[QTL], mt[QTL];  // reference max and reference + kGrow
 #pragma unroll
@@ -133,7 +175,10 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     // Copy (a0 % 4) of the table is shifted so that the lane's 8 floats start
     // on a 16-byte boundary.
     const int a0 = (qy[j] - 4 * (BPC - 1) - g4 + M - 1) * R + (M - 1 - qx[j]);
-    tb[j] = (lds_f4)(rt4 + (a0 & 3) * TS + (a0 & ~3));
+    if constexpr (T1)
+      tbf[j] = (lds_f)(rt4 + a0);
+    else
+      tb[j] = (lds_f4)(rt4 + (a0 & 3) * TS + (a0 & ~3));
     o0[j] = o1[j] = ls[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[j] = -1e30f;
     mt[j] = -1e30f;
@@ -146,16 +191,27 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
   // this base plus an immediate (the static LDS offsets of the arrays are not
   // folded into the immediates, which would overflow their 16 bits), and so
   // that the ones operand stays in vector registers.
-  lds_q8 kl = (lds_q8)&ks[(8 * (i16 >> 2) + (i16 & 3)) * LDK + g4 * 8];
-  lds_v4s vl = (lds_v4s)&vs[(8 * g4 + (i16 >> 2)) * LDK + 8 * (i16 & 3)];
+  // Swizzled rows: for the K reads (row/8) % 4 = l%16 / 4, for the V reads
+  // (row/8) % 4 = l/16, whatever the block.
+  lds_q8 kl = SWZ ? (lds_q8)&ks[(8 * (i16 >> 2) + (i16 & 3)) * LDK + ((g4 ^ (i16 >> 2)) << 3)]
+                  : (lds_q8)&ks[(8 * (i16 >> 2) + (i16 & 3)) * LDK + g4 * 8];
+  lds_v4s vl = SWZ ? (lds_v4s)&vs[(8 * g4 + (i16 >> 2)) * LDK + (((i16 & 3) ^ g4) << 3)]
+                   : (lds_v4s)&vs[(8 * g4 + (i16 >> 2)) * LDK + 8 * (i16 & 3)];
   asm volatile("" : "+v"(kl), "+v"(vl), "+v"(ones));
 #pragma unroll
-  for (int j = 0; j < QTL; ++j) asm volatile("" : "+v"(tb[j]));
+  for (int j = 0; j < QTL; ++j) {
+    if constexpr (T1)
+      asm volatile("" : "+v"(tbf[j]));
+    else
+      asm volatile("" : "+v"(tb[j]));
+  }
   lds_f4 ninf4 = (lds_f4)ninf;
 
   // Key blocks of 32: block kbi is chunk kbi / BPC, rows 4b .. 4b+3 with
   // b = kbi % BPC.  Fully unrolled, with the LDS operands of the next block
-  // (K and V fragments, the tiles' biases) loaded while this one is computed.
+  // (K and V fragments; with four table copies also the tiles' biases) loaded
+  // while this one is computed; with one table copy the biases are read at
+  // the block's start (fewer registers).
   constexpr int NB = N / 32;
   struct Ops {
     vec8<QT> k0, k1;
@@ -164,17 +220,20 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     bool act[QTL];       // tile has an allowed key in this block (masked windows)
     unsigned bits[QTL];  // allowed keys of the lane's group (masked windows)
   };
-  auto load = [&](int kbi, Ops& op) {
-    const int ck = kbi / BPC, b = kbi - ck * BPC;
+  auto load_kv = [&](int kbi, Ops& op) {
     const int kb = 32 * kbi;
     op.k0 = kl[kb * LDK / 8];
     op.k1 = kl[(kb + 4) * LDK / 8];
-    op.v0 = vt_frag<VT>(vl, kb, 0);
-    op.v1 = vt_frag<VT>(vl, kb, 1);
+    op.v0 = vt_frag<VT, LDK>(vl, kb, 0);
+    op.v1 = vt_frag<VT, LDK>(vl, kb, 1);
+  };
+  auto load_bias = [&](int kbi, Ops& op) {
+    const int ck = kbi / BPC, b = kbi - ck * BPC;
     const int boff = 8 * ck + 4 * R * (BPC - 1 - b);
 #pragma unroll
     for (int j = 0; j < QTL; ++j) {
       lds_f4 bp = tb[j] + boff / 4;
+      lds_f bpf = tbf[j] + boff;
       op.act[j] = true;
       op.bits[j] = 0xffu;
       if constexpr (MASKED) {
@@ -186,19 +245,36 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
         const bool yok = !my || ((ky < bnd) == (qy[j] < bnd));
         op.bits[j] = yok ? xb : 0u;
         op.act[j] = __any(op.bits[j] != 0u);  // else the tile is masked in this block
-        if (op.bits[j] == 0u) bp = ninf4;
+        if (op.bits[j] == 0u) {
+          bp = ninf4;
+          bpf = (lds_f)ninf4;
+        }
       }
-      op.b0[j] = bp[0];
-      op.b1[j] = bp[1];
+      if constexpr (T1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          op.b0[j][r] = bpf[r];
+          op.b1[j][r] = bpf[4 + r];
+        }
+      } else {
+        op.b0[j] = bp[0];
+        op.b1[j] = bp[1];
+      }
     }
   };
 
   Ops cur;
-  load(0, cur);
+  load_kv(0, cur);
+  if constexpr (!T1) load_bias(0, cur);
 #pragma unroll
   for (int kbi = 0; kbi < NB; ++kbi) {
+    hook(kbi);
+    if constexpr (T1) load_bias(kbi, cur);
     Ops nxt;
-    if (kbi + 1 < NB) load(kbi + 1, nxt);
+    if (kbi + 1 < NB) {
+      load_kv(kbi + 1, nxt);
+      if constexpr (!T1) load_bias(kbi + 1, nxt);
+    }
     const int ck = kbi / BPC;
     bool straddle = false;
     if constexpr (MASKED) {
