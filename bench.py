@@ -68,6 +68,7 @@ def stage_work(case):
         "proj_tiled_kernel": (2 * C * C * T, T * 2 * C * e + C * C * e),
         "window_attn_kernel": (4 * N * C * T, T * (2 * C * eqk + C * e + C * e) + tab),
         "tiled_attn_kernel": (4 * N * C * T, T * (2 * C * eqk + C * e + C * e) + tab),
+        "w8_attn_kernel": (4 * N * C * T, T * (2 * C * eqk + C * e + C * e) + tab),
         "proj_gemm_kernel": (2 * C * C * T, T * 2 * C * e + C * C * e),
     }
 
@@ -184,7 +185,8 @@ class Runner:
 KERNEL_SOURCE = {
     "fused_window_kernel": "fused_window.hip", "fused_w8_kernel": "fused_w8.hip",
     "fused_w16_kernel": "fused_w16.hip", "tiled_attn_kernel": "tiled_attn.hip",
-    "window_attn_kernel": "window_attn.hip", "qkv_tiled_kernel": "gemm_tiled.hip",
+    "window_attn_kernel": "window_attn.hip", "w8_attn_kernel": "w8_attn.hip",
+    "qkv_tiled_kernel": "gemm_tiled.hip",
     "proj_tiled_kernel": "gemm_tiled.hip", "qkv_gemm_kernel": "gemm.hip",
     "proj_gemm_kernel": "gemm.hip",
 }

@@ -194,7 +194,10 @@ static const char* stage_name(const swin_wmsa_desc* d, int i) {
   if (plan == kPlanFusedW8) return "fused_w8_kernel";
   const bool tg = use_tiled_gemm(d);
   if (i == 0) return tg ? "qkv_tiled_kernel" : "qkv_gemm_kernel";
-  if (i == 1) return plan == kPlanTiled ? "tiled_attn_kernel" : "window_attn_kernel";
+  if (i == 1)
+    return plan == kPlanTiled                         ? "tiled_attn_kernel"
+           : w8_attn_supported(d->M, io_type(d)) ? "w8_attn_kernel"
+                                                   : "window_attn_kernel";
   return tg ? "proj_tiled_kernel" : "proj_gemm_kernel";
 }
 constexpr int kMaxStages = 3;
@@ -282,7 +285,9 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
   if (err == hipSuccess) err = tg ? launch_qkv_tiled(p, hs) : launch_qkv_gemm(p, hs);
   if (err == hipSuccess) err = mark(1);
   if (err == hipSuccess)
-    err = plan == kPlanTiled ? launch_tiled_attn(p, hs) : launch_window_attn(p, hs);
+    err = plan == kPlanTiled                    ? launch_tiled_attn(p, hs)
+          : w8_attn_supported(p.g.M, p.io) ? launch_w8_attn(p, hs)
+                                           : launch_window_attn(p, hs);
   if (err == hipSuccess) err = mark(2);
   if (err == hipSuccess) err = tg ? launch_proj_tiled(p, hs) : launch_proj_gemm(p, hs);
   if (err == hipSuccess) err = mark(3);

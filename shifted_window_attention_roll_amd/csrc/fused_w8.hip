@@ -30,100 +30,12 @@
 // window's token rows right after its attention; with 4 heads it reloads
 // weights and rows per window.  A second barrier (after the next window's q)
 // keeps the K stores behind every wave's projection reads.
-#include "attn_core.hpp"
 #include "launch.hpp"
+#include "w8_core.hpp"
 
 namespace swin {
 
 namespace {
-
-// Reversed bias table per head: entry [a][c] (rows of 16 floats) is the bias
-// (times log2 e) of dy = a - 7, dx = 7 - c; -inf outside the window's range
-// and in the kPadInf entries after the 15 rows (read by padded key rows).
-constexpr int kTabRows = 15 * 16;
-constexpr int kPadInf = 3 * 32 + 8;
-constexpr int kTab = kTabRows + kPadInf;
-
-typedef __attribute__((address_space(3))) const float* lds_f;
-
-template <typename QT, typename T, int MV, bool MASKED>
-__device__ __forceinline__ void w8_attend(const vec8<QT> (&qf)[4], const vec8<QT> (&kf)[2][2],
-                                          const vec8<T> (&vf)[2][2], lds_f tb0,
-                                          lds_f tb1, int qy0, int qx, int g4, int bnd,
-                                          bool my, bool mx, T* os) {
-  const float NEG_INF = -__builtin_inff();
-  vec8<T> ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = from_f32<T>(1.0f);
-  // Shifted windows: allowed key columns of the lane's query column.
-  unsigned xbits = 0xffu;
-  if (MASKED && mx) {
-    const unsigned lm = (1u << bnd) - 1u;
-    xbits = qx < bnd ? lm : (~lm & 0xffu);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // Logits of the lane's query (slot 16j + l%16) against keys 32b + 8g + e:
-    // key row 4b + g, column e.  Bias = initial accumulator.
-    f32x4 s[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const lds_f tb = (b ? tb1 : tb0) + 32 * j;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[b][t][r] = tb[4 * t + r];
-    }
-    if constexpr (MASKED) {
-      const int qy = 2 * j + qy0;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int ky = 4 * b + g4;
-        const bool yok = !my || ((qy < bnd) == (ky < bnd));
-        const unsigned bits = yok ? xbits : 0u;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (!((bits >> (4 * t + r)) & 1u)) s[b][t][r] = NEG_INF;
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) s[b][t] = mma_16x16x32(kf[b][t], qf[j], s[b][t]);
-    // Exact row max over the 64 keys (column 7 is padding for side 7).
-    float m = NEG_INF;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < MV) m = fmaxf(m, s[b][e >> 2][e & 3]);
-    m = xor32_max(xor16_max(m));
-    if constexpr (MASKED) m = m == NEG_INF ? 0.f : m;  // padded query with no allowed key
-    f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, l = o0;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      vec8<T> pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pf[e] = e < MV ? from_f32<T>(fast_exp2(s[b][e >> 2][e & 3] - m)) : from_f32<T>(0.f);
-      o0 = mma_16x16x32(vf[b][0], pf, o0);
-      o1 = mma_16x16x32(vf[b][1], pf, o1);
-      l = mma_16x16x32(ones, pf, l);
-    }
-    const float inv = __builtin_amdgcn_rcpf(l[0]);
-    vec8<T> of;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      of[r] = from_f32<T>(o0[r] * inv);
-      of[4 + r] = from_f32<T>(o1[r] * inv);
-    }
-    // O of the lane's query, dims 8g .. 8g+7: into the wave's K rows, whose
-    // fragments are all in registers already.
-    store8(os + 16 * j * kAttnLD, of);
-  }
-}
 
 // Waves per SIMD the kernel is compiled for: with up to 3 heads the wave keeps
 // all of its weights in registers across windows (2 waves per SIMD at 2 and 3
@@ -156,15 +68,7 @@ void fused_w8_kernel(FwdParams p, int n_windows) {
   T* y = static_cast<T*>(p.y);
   const float NEG_INF = -__builtin_inff();
 
-  constexpr int R = 2 * MV - 1;
-  for (int i = tid; i < HEADS * kTab; i += NT) {
-    const int hh = i / kTab, e = i - hh * kTab;
-    const int dy = (e >> 4) - 7, dx = 7 - (e & 15);
-    float v = NEG_INF;
-    if (e < kTabRows && dy > -MV && dy < MV && dx > -MV && dx < MV)
-      v = p.table[(int64_t)((dy + MV - 1) * R + dx + MV - 1) * HEADS + hh] * kLog2e;
-    tabs[hh][e] = v;
-  }
+  for (int hh = 0; hh < HEADS; ++hh) fill_w8_table<MV>(tabs[hh], p.table, HEADS, hh, tid, NT);
   {
     const T* bq = static_cast<const T*>(p.b_qkv);
     const T* bp = static_cast<const T*>(p.b_proj);
@@ -341,11 +245,14 @@ void fused_w8_kernel(FwdParams p, int n_windows) {
         kf[b][t] = kl[(32 * b + 4 * t) * LDK / 8];
         vf[b][t] = vt_frag<T>(vl, 32 * b, t);
       }
+    // O of query tile j into the wave's K rows (their fragments are all in
+    // registers already).
     T* os = reinterpret_cast<T*>(ks[h]) + i16 * LDK + 8 * g4;
+    auto store_o = [&](int j, const vec8<T>& of) { store8(os + 16 * j * LDK, of); };
     if (my || mx)
-      w8_attend<QT, T, MV, true>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, my, mx, os);
+      w8_attend<QT, T, MV, true>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, my, mx, store_o);
     else
-      w8_attend<QT, T, MV, false>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, false, false, os);
+      w8_attend<QT, T, MV, false>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, false, false, store_o);
     // The next window's token rows, in flight across the barrier and the
     // projection.
     int cur[4];

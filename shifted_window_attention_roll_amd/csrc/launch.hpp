@@ -62,6 +62,10 @@ hipError_t launch_proj_tiled(const FwdParams& p, hipStream_t st);
 // 16-bit I/O (needs chunked slots).
 bool fused_w16_supported(int M, int C, int heads, int io);
 hipError_t launch_fused_w16(const FwdParams& p, hipStream_t st);
+// Attention for window side 7 with 16-bit I/O between the GEMMs (row-major
+// slots).
+bool w8_attn_supported(int M, int io);
+hipError_t launch_w8_attn(const FwdParams& p, hipStream_t st);
 // Single-kernel forward for window sides 7 and 8 with C = 32 * heads,
 // heads <= 4, 16-bit I/O (its own 8 x 8 slot layout).
 bool fused_w8_supported(int M, int C, int heads, int io);

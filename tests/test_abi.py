@@ -145,8 +145,12 @@ def test_kernel_names_and_timed_rejects(lib):
                                    dtype=torch.bfloat16, mode="v2")) == ["fused_w8_kernel"]
     assert swin.kernel_names(_desc(dtype=torch.float32)) == ["fused_window_kernel"]
     assert swin.kernel_names(_desc(H=48, W=48, M=6, s=3)) == ["fused_window_kernel"]
-    assert swin.kernel_names(_desc(C=512, heads=16)) == ["qkv_tiled_kernel", "window_attn_kernel",
+    assert swin.kernel_names(_desc(C=512, heads=16)) == ["qkv_tiled_kernel", "w8_attn_kernel",
                                                           "proj_tiled_kernel"]
+    assert swin.kernel_names(_desc(C=512, heads=16, dtype=torch.float32)) == [
+        "qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"]
+    assert swin.kernel_names(_desc(H=14, W=14, C=160, heads=5)) == [
+        "qkv_gemm_kernel", "w8_attn_kernel", "proj_gemm_kernel"]
     assert swin.kernel_names(_desc(H=48, W=48, M=12, s=6, C=128, heads=4)) == three
     assert swin.kernel_names(_desc(H=48, W=48, M=12, s=6, C=256, heads=8)) == [
         "qkv_tiled_kernel", "window_attn_kernel", "proj_tiled_kernel"]

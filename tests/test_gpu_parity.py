@@ -106,6 +106,9 @@ SMALL = [
     (2, 16, 16, 128, 4, 8, 4, "bf16", "v2", 0.1),     # 4 heads: weights reloaded per window
     (2, 16, 16, 64, 2, 8, 4, "bf16", "v2", 0.1),
     (3, 14, 21, 96, 3, 7, 3, "bf16", "v1", 0.1),     # 18 windows
+    # window 7 between the GEMMs (more than 4 heads): one wave per (window, head)
+    (1, 14, 21, 192, 6, 7, 3, "bf16", "v2", 0.1),
+    (2, 21, 14, 160, 5, 7, 5, "fp16", "v1", 0.3),
     (1, 21, 14, 96, 3, 7, 5, "bf16", "v2", 0.1),     # H != W, split 2
     (2, 24, 16, 64, 2, 8, 1, "fp16", "v1", 0.1),     # split 7
     (1, 7, 7, 96, 3, 7, 3, "fp16", "v1", 0.3),       # window = image, shifted
