@@ -63,7 +63,8 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
   __shared__ float bqs[3 * C], bps[C];  // linear biases
 
   const Geom& g = p.g;
-  const int w = blockIdx.x;  // window
+  const int n_windows = g.B * g.nW;
+  int w = blockIdx.x;  // window (persistent: then w + gridDim.x, ...)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g4 = lane >> 4, i16 = lane & 15;
@@ -85,17 +86,8 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
   int tile[QTL];
 #pragma unroll
   for (int j = 0; j < QTL; ++j) tile[j] = QTL * wave + j;
-  const int wl = w % g.nW;
-  const int wy = wl / g.nWx, wx = wl - (wl / g.nWx) * g.nWx;
-  const bool my = g.s > 0 && wy == g.H / M - 1;
-  const bool mx = g.s > 0 && wx == g.nWx - 1;
   const float eps2 = p.eps * p.eps;
-
   f32x4 yacc[QTL][CT];
-#pragma unroll
-  for (int j = 0; j < QTL; ++j)
-#pragma unroll
-    for (int c = 0; c < CT; ++c) yacc[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Weight-row permutation inside a 32-row pair of 16-row tiles: fragment t's
   // row i16 is row 8*(i16/4) + 4t + i16%4, so that output lanes hold 8
@@ -107,7 +99,10 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
   // head's start).
   constexpr int WPT = (96 * XCH + NT - 1) / NT;   // 16-byte weight chunks per thread
   constexpr int PPT = (CT * 64 + NT - 1) / NT;    // 16-byte projection chunks per thread
-  constexpr int TPT = (4 * TS + NT - 1) / NT;     // table floats per thread
+  // Copy c of the table holds element p + c at position p, so elements
+  // 0 .. TS + 2 cover all four: each is loaded once and stored up to 4 times.
+  constexpr int TE = TS + 3;
+  constexpr int TPT = (TE + NT - 1) / NT;         // table elements per thread
   constexpr int R = 2 * M - 1;
   uint4 wreg[WPT], preg[PPT];
   float treg[TPT];
@@ -131,11 +126,9 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
     }
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
-      const int i = tid + k * NT;
-      const int c = i / TS, e = i - c * TS + c;  // copy c holds element e at i - c*TS
-      treg[k] = (i < 4 * TS && e < R * R)
-                    ? p.table[(int64_t)((e / R) * R + (R - 1 - e % R)) * HEADS + hh] * kLog2e
-                    : -__builtin_inff();
+      const int e = tid + k * NT;
+      treg[k] = e < R * R ? p.table[(int64_t)((e / R) * R + (R - 1 - e % R)) * HEADS + hh] * kLog2e
+                          : -__builtin_inff();
     }
   };
   auto store_head = [&]() {
@@ -154,20 +147,69 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
     }
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
-      const int i = tid + k * NT;
-      if (i < 4 * TS) rt4[i] = treg[k];
+      const int e = tid + k * NT;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (e - c >= 0 && e - c < TS) rt4[c * TS + e - c] = treg[k];
     }
   };
+  // Shift + partition map.  A window's origin (uniform): its image's first
+  // token and its first row and column in the shifted frame.  Slot t (chunks
+  // of 8 columns x 16 rows) is row (t % 128) / 8, column 8 (t / 128) + t % 8
+  // of the window; rows and columns past the image wrap around.
+  struct Origin {
+    int64_t base;
+    int y0, x0;
+  };
+  auto origin = [&](int win) {
+    const int b = (int)fdiv((uint32_t)win, g.dnW);
+    const int wl = win - b * g.nW;
+    const int wy = (int)fdiv((uint32_t)wl, g.dnWx);
+    return Origin{(int64_t)b * g.H * g.W, wy * M + g.s, (wl - wy * g.nWx) * M + g.s};
+  };
+  auto token = [&](const Origin& o, int t) -> int64_t {
+    int yy = o.y0 + ((t & 127) >> 3);
+    if (yy >= g.H) yy -= g.H;
+    int xx = o.x0 + ((t >> 7) << 3) + (t & 7);
+    if (xx >= g.W) xx -= g.W;
+    return o.base + (int64_t)__umul24(yy, g.W) + xx;
+  };
+  // Window rows: chunk c of this thread is row (tid + c*NT) / XCH, 16-byte
+  // column (tid + c*NT) % XCH.
+  constexpr int CHX = N * XCH / NT;
+  static_assert(CHX * NT == N * XCH, "gather split");
+  auto x_src = [&](const Origin& o, int c) {
+    int i = tid + c * NT;
+    asm volatile("" : "+v"(i));  // address computed where it is used, not kept live
+    const int r = i / XCH;
+    return x + token(o, r) * C + 8 * (i - r * XCH);
+  };
+  auto x_dst = [&](int c) {
+    const int i = tid + c * NT, r = i / XCH;
+    return &xs[r * LDX + 8 * (i - r * XCH)];
+  };
   fetch_head(0);  // in flight together with the window rows
-  // Window rows, gathered through the shift + partition map.
-  for (int i = tid; i < N * XCH; i += NT) {
-    const int r = i / XCH, c = i - r * XCH;
-    *reinterpret_cast<uint4*>(&xs[r * LDX + 8 * c]) =
-        gload16(x + src_token(g, w * N + r) * C + 8 * c);
-  }
+#pragma unroll
+  for (int c = 0; c < CHX; ++c)
+    *reinterpret_cast<uint4*>(x_dst(c)) = gload16(x_src(origin(w), c));
+
+  for (; w < n_windows; w += gridDim.x) {
+  const int nxt = w + gridDim.x;
+  const bool more = nxt < n_windows;
+  const Origin org = origin(w), org_n = origin(nxt);
+  const int wl = w % g.nW;
+  const int wy = wl / g.nWx, wx = wl - (wl / g.nWx) * g.nWx;
+  const bool my = g.s > 0 && wy == g.H / M - 1;
+  const bool mx = g.s > 0 && wx == g.nWx - 1;
+#pragma unroll
+  for (int j = 0; j < QTL; ++j)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) yacc[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int h = 0; h < HEADS; ++h) {
-    if (h > 0) __syncthreads();  // every wave is done with the previous head's table
+    // Every wave is done with the previous head's weights and table (and, at
+    // a window's first head, the previous window's rows are all in LDS).
+    __syncthreads();
     // 1. This head's q, k, v weight rows and bias-table copies; the next
     //    head's are fetched while this one is computed.
     store_head();
@@ -237,18 +279,45 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
     }
     __syncthreads();
 
-    // The next head's weights and table are fetched while this one's
-    // attention runs (no other global loads are in flight then, so the
-    // projection's weight loads below do not wait behind them).
-    if (h + 1 < HEADS) fetch_head(h + 1);
+    // The next head's (or the next window's first head's) weights and table
+    // are fetched while this one's attention runs.
+    const bool last = h + 1 == HEADS;
+    if (!last)
+      fetch_head(h + 1);
+    else if (more)
+      fetch_head(0);
 
-    // 3. Attention of the wave's two query tiles.
+    // 3. Attention of the wave's two query tiles.  During the window's last
+    //    head (every wave is past its last read of the rows) the next
+    //    window's rows go into LDS, one 16-byte chunk per key block or two:
+    //    chunk c is loaded at block (c * NB) / CHX and stored when the next
+    //    one is loaded.
+    constexpr int NB = N / 32;
+    uint4 pend = {0, 0, 0, 0};
+    auto hook = [&](int kbi) {
+      if (!(last && more)) return;
+#pragma unroll
+      for (int c = 0; c < CHX; ++c) {
+        if ((c * NB) / CHX == kbi) {
+          // Keep each chunk's load in its own key block (not hoisted together).
+          __builtin_amdgcn_sched_barrier(0);
+          if (c > 0) *reinterpret_cast<uint4*>(x_dst(c - 1)) = pend;
+          pend = gload16(x_src(org_n, c));
+        }
+      }
+    };
     float o[QTL][8];
+    // Opaque here, so that the per-block mask values derived from it are
+    // computed in the blocks rather than hoisted out of the loops (which
+    // runs out of scalar registers).
+    int bnd = M - g.s;
+    asm volatile("" : "+s"(bnd));
     if (my || mx)
-      attn_tiles<QT, T, M, QTL, true>(qf, tile, ks, vs, rt4, ninf, lane, M - g.s, my, mx, o);
+      attn_tiles<QT, T, M, QTL, true>(qf, tile, ks, vs, rt4, ninf, lane, bnd, my, mx, o, hook);
     else
-      attn_tiles<QT, T, M, QTL, false>(qf, tile, ks, vs, rt4, ninf, lane, M - g.s, false, false,
-                                       o);
+      attn_tiles<QT, T, M, QTL, false>(qf, tile, ks, vs, rt4, ninf, lane, bnd, false, false, o,
+                                       hook);
+    if (last && more) *reinterpret_cast<uint4*>(x_dst(CHX - 1)) = pend;
 
     // 4. Y^T += Wp[:, h*32 .. +31] O_h^T (fragments from LDS); the Wp rows of
     //    each channel-tile pair are interleaved like the QKV weight rows.
@@ -267,7 +336,7 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
   T* y = static_cast<T*>(p.y);
 #pragma unroll
   for (int j = 0; j < QTL; ++j) {
-    const int64_t dst = src_token(g, w * N + 16 * tile[j] + i16) * C;
+    const int64_t dst = token(org, 16 * tile[j] + i16) * C;
 #pragma unroll
     for (int cp = 0; cp < CT / 2; ++cp) {
       float v[8];
@@ -280,11 +349,18 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
       gstore16(y + dst + 32 * cp + 8 * g4, __builtin_bit_cast(uint4, to_vec8<T>(v, 1.0f)));
     }
   }
+  }  // windows
 }
 
 template <typename T, typename QT, bool V2>
 hipError_t w16_heads(const FwdParams& p, hipStream_t st) {
-  const dim3 grid(p.g.B * p.g.nW), block(64 * kW16Waves);
+  // Persistent: one workgroup per CU (the LDS holds one), each walking
+  // windows with the grid as stride.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int n = p.g.B * p.g.nW;
+  const dim3 grid(n < cus ? n : cus), block(64 * kW16Waves);
   switch (p.g.heads) {
     case 1: hipLaunchKernelGGL((fused_w16_kernel<T, QT, 1, V2>), grid, block, 0, st, p); break;
     case 2: hipLaunchKernelGGL((fused_w16_kernel<T, QT, 2, V2>), grid, block, 0, st, p); break;
