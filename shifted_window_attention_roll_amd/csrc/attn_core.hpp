@@ -133,10 +133,14 @@ __device__ __forceinline__ vec8<VT> vt_frag(lds_v4s vl, int kb, int t) {
 // O for the lane's query and d = 8*(l/16) + e, e = 0..7.  LAYOUT / TABLE pick
 // the K, V layout and the bias-table mode; hook(kbi) runs at the start of key
 // block kbi (the caller's work to interleave, e.g. staging the next item).
+// With FAST and !MASKED, returns false (o undefined) when the fixed-reference
+// pass saw a logit too far above its reference; the caller then runs the
+// MASKED instance with my = mx = false, which is exact for any logits.
+// Otherwise returns true.
 template <typename QT, typename VT, int M, int QTL, bool MASKED,
           KvLayout LAYOUT = KvLayout::kPadded, TableMode TABLE = TableMode::kTable4,
-          class Hook = NoHook>
-__device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int (&tile)[QTL],
+          bool FAST = true, class Hook = NoHook>
+__device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int (&tile)[QTL],
                                            const QT* ks, const VT* vs, const float* rt4,
                                            const float* ninf, int lane, int bnd, bool my, bool mx,
                                            float (&o)[QTL][8], Hook hook = Hook()) {
@@ -280,8 +284,21 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     if constexpr (MASKED) {
       const int left = min(max(bnd - 8 * ck, 0), 8);
       straddle = mx && left > 0 && left < 8;
+      // Skip the block when every tile is masked in it.  Otherwise every tile
+      // is computed: a masked tile's logits are -inf (its bias reads the -inf
+      // strip), so its P is 0 and it adds nothing.  The wave's tiles share
+      // a column chunk and usually a row region, so they are masked together.
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < QTL; ++j) any = any || cur.act[j];
+      if (!any) {
+        if (kbi + 1 < NB) cur = nxt;
+        continue;
+      }
     }
-    // Phase 1, every tile: S^T = K Q^T on top of the bias, block max.
+    // Phase 1, every tile: S^T = K Q^T on top of the bias, block max (with
+    // the fixed reference, only in block 0).
+    constexpr bool FIXED = FAST && !MASKED;
     f32x4 s0[QTL], s1[QTL];
     float bm[QTL];
 #pragma unroll
@@ -297,21 +314,30 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
             if (!((bits >> (4 + r)) & 1u)) s1[j][r] = NEG_INF;
           }
         }
-        if (!cur.act[j]) {
-          bm[j] = NEG_INF;
-          continue;
-        }
       }
       s0[j] = mma_16x16x32(cur.k0, qf[j], s0[j]);
       s1[j] = mma_16x16x32(cur.k1, qf[j], s1[j]);
-      bm[j] = fmaxf(fmaxf(fmaxf(s0[j][0], s0[j][1]), fmaxf(s0[j][2], s0[j][3])),
-                    fmaxf(fmaxf(s1[j][0], s1[j][1]), fmaxf(s1[j][2], s1[j][3])));
+      if (!FIXED || kbi == 0)
+        bm[j] = fmaxf(fmaxf(fmaxf(s0[j][0], s0[j][1]), fmaxf(s0[j][2], s0[j][3])),
+                      fmaxf(fmaxf(s1[j][0], s1[j][1]), fmaxf(s1[j][2], s1[j][3])));
     }
-    // Phase 2, rare: some lane of some tile saw a logit more than kGrow above
-    // its reference; move every tile's reference to its row max.
-    uint64_t grow = 0;
+    // Phase 2.  Unmasked windows with FAST: the reference is the row max of
+    // block 0 and never moves -- no per-block max, compare or branch; the
+    // row sums are checked once at the end.  Otherwise (masked windows, where
+    // a row may have no allowed key in block 0, the fallback, and !FAST)
+    // lazy: when some lane of some tile saw a logit more than kGrow above its
+    // reference, every tile's reference moves to its row max.
+    if constexpr (FIXED) {
+      if (kbi == 0) {
 #pragma unroll
-    for (int j = 0; j < QTL; ++j) grow |= __builtin_amdgcn_ballot_w64(bm[j] > mt[j]);
+        for (int j = 0; j < QTL; ++j) m[j] = xor32_max(xor16_max(bm[j]));
+      }
+    }
+    uint64_t grow = 0;
+    if constexpr (!FIXED) {
+#pragma unroll
+      for (int j = 0; j < QTL; ++j) grow |= __builtin_amdgcn_ballot_w64(bm[j] > mt[j]);
+    }
     if (grow) {
 #pragma unroll
       for (int j = 0; j < QTL; ++j) {
@@ -328,9 +354,6 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     // Phase 3, every tile: P = exp2(S - m), O^T += V^T P^T, row sums.
 #pragma unroll
     for (int j = 0; j < QTL; ++j) {
-      if constexpr (MASKED) {
-        if (!cur.act[j]) continue;
-      }
       vec8<VT> pf;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -344,6 +367,18 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     if (kbi + 1 < NB) cur = nxt;
   }
 
+  if constexpr (FAST && !MASKED) {
+    // Every P is at most its row sum, and the reference is at most the row
+    // max (P of the largest logit >= 1).  A row sum below kFixedLimit (also
+    // false for inf / NaN) means no P went past it: bfloat16 P stays far
+    // from its overflow, float16 P below 65504.  Otherwise the caller redoes
+    // the item on the lazy path.
+    constexpr float kFixedLimit = __is_same(VT, h16) ? 32768.0f : 18446744073709551616.0f;
+    bool far = false;
+#pragma unroll
+    for (int j = 0; j < QTL; ++j) far = far || !(ls[j][0] < kFixedLimit);
+    if (__builtin_amdgcn_ballot_w64(far)) return false;
+  }
   // Fragment pair t row 4*g4 + r is head dim 8*g4 + 4t + r.
 #pragma unroll
   for (int j = 0; j < QTL; ++j) {
@@ -354,6 +389,7 @@ __device__ __forceinline__ void attn_tiles(const vec8<QT> (&qf)[QTL], const int 
       o[j][4 + r] = o1[j][r] * inv;
     }
   }
+  return true;
 }
 
 }  // namespace swin

@@ -45,15 +45,14 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
   constexpr int M = 16, N = 256, D = 32;
   constexpr int C = 32 * HEADS;
   constexpr int LDX = C + 8;  // x rows (16-byte padded)
-  constexpr int LDK = kAttnLD;
   constexpr int TS = table_stride<M>();
   constexpr int QTL = 2;      // 16-token tiles per wave
   constexpr int NT = 64 * kW16Waves;
   constexpr int CT = C / 16;  // output channel tiles
   __shared__ __attribute__((aligned(16))) T xs[N * LDX];
   __shared__ __attribute__((aligned(16))) T ws[96 * LDX];
-  __shared__ __attribute__((aligned(16))) QT ks[N * LDK];
-  __shared__ __attribute__((aligned(16))) T vs[N * LDK];
+  __shared__ __attribute__((aligned(16))) QT ks[N * 32];  // swizzled rows (attn_core.hpp)
+  __shared__ __attribute__((aligned(16))) T vs[N * 32];
   __shared__ __attribute__((aligned(16))) float rt4[4 * TS];
   __shared__ __attribute__((aligned(16))) float ninf[8];
   // The head's projection columns Wp[:, h*32 .. +31] in fragment order:
@@ -272,9 +271,9 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
         if (pt == 0)
           qf[j] = to_vec8<QT>(v, mult);
         else if (pt == 1)
-          *reinterpret_cast<vec8<QT>*>(&ks[row * LDK + 8 * g4]) = to_vec8<QT>(v, mult);
+          *reinterpret_cast<vec8<QT>*>(&ks[kv_swz(row, g4)]) = to_vec8<QT>(v, mult);
         else
-          *reinterpret_cast<vec8<T>*>(&vs[row * LDK + 8 * g4]) = to_vec8<T>(v, 1.0f);
+          *reinterpret_cast<vec8<T>*>(&vs[kv_swz(row, g4)]) = to_vec8<T>(v, 1.0f);
       }
     }
     __syncthreads();
@@ -312,11 +311,16 @@ __global__ __launch_bounds__(64 * kW16Waves, 1) void fused_w16_kernel(FwdParams 
     // runs out of scalar registers).
     int bnd = M - g.s;
     asm volatile("" : "+s"(bnd));
-    if (my || mx)
-      attn_tiles<QT, T, M, QTL, true>(qf, tile, ks, vs, rt4, ninf, lane, bnd, my, mx, o, hook);
-    else
-      attn_tiles<QT, T, M, QTL, false>(qf, tile, ks, vs, rt4, ninf, lane, bnd, false, false, o,
-                                       hook);
+    // Unmasked windows take the fixed-reference pass; masked ones, and the
+    // rare item whose row sums outgrow it, the exact lazy one (running the
+    // hook twice stores the same rows twice).
+    bool done = false;
+    if (!(my || mx))
+      done = attn_tiles<QT, T, M, QTL, false, KvLayout::kSwizzled>(qf, tile, ks, vs, rt4, ninf,
+                                                                   lane, bnd, false, false, o, hook);
+    if (!done)
+      attn_tiles<QT, T, M, QTL, true, KvLayout::kSwizzled>(qf, tile, ks, vs, rt4, ninf, lane, bnd,
+                                                           my, mx, o, hook);
     if (last && more) *reinterpret_cast<uint4*>(x_dst(CHX - 1)) = pend;
 
     // 4. Y^T += Wp[:, h*32 .. +31] O_h^T (fragments from LDS); the Wp rows of

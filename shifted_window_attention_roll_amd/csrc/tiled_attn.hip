@@ -18,8 +18,14 @@ namespace swin {
 
 namespace {
 
+// Waves per SIMD the launch below keeps resident (workgroups per CU x WAVES / 4).
+template <int M>
+constexpr int tiled_waves_per_simd() { return M == 24 ? 3 : 4; }
+
 template <typename QT, typename VT, int M, int QTL, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void tiled_attn_kernel(FwdParams p, int n_items) {
+__global__ __launch_bounds__(64 * WAVES)
+__attribute__((amdgpu_waves_per_eu(tiled_waves_per_simd<M>())))
+void tiled_attn_kernel(FwdParams p, int n_items) {
   constexpr int D = 32;
   constexpr int N = M * M;
   static_assert(M % 8 == 0 && N / 16 == QTL * WAVES, "tile split");
@@ -100,13 +106,17 @@ __global__ __launch_bounds__(64 * WAVES) void tiled_attn_kernel(FwdParams p, int
       }
     };
 
+    // Unmasked windows take the fast path; masked ones, and the rare item
+    // whose logits outgrow the fast path's reference, the exact lazy one
+    // (running the hook twice stages the same chunks twice).
     float o[QTL][8];
-    if (my || mx)
+    bool done = false;
+    if (!(my || mx))
+      done = attn_tiles<QT, VT, M, QTL, false, KvLayout::kSwizzled, TableMode::kTable1>(
+          qf, tile, ks[buf], vs[buf], rt, ninf, lane, M - g.s, false, false, o, hook);
+    if (!done)
       attn_tiles<QT, VT, M, QTL, true, KvLayout::kSwizzled, TableMode::kTable1>(
           qf, tile, ks[buf], vs[buf], rt, ninf, lane, M - g.s, my, mx, o, hook);
-    else
-      attn_tiles<QT, VT, M, QTL, false, KvLayout::kSwizzled, TableMode::kTable1>(
-          qf, tile, ks[buf], vs[buf], rt, ninf, lane, M - g.s, false, false, o, hook);
 
     // O rows in slot order, columns h*32 + d: the lane's 8 dims, one store.
     VT* og = static_cast<VT*>(p.buf.o);

@@ -129,6 +129,28 @@ def test_wmsa_small(gpu, B, H, W, C, heads, M, s, dtype, mode, bias_std):
     helpers.assert_close(workloads.f64(y.cpu()), ref, dtype, "small")
 
 
+# Relative-position biases far larger than the logits' usual spread: rows
+# whose largest logit lies well past their first key block's, so the
+# attention core's fixed-reference pass hands over to its exact lazy pass
+# (kGrow = 8 in base 2 with float16 P, 64 with bfloat16 P).
+@pytest.mark.parametrize("B,H,W,C,heads,M,s,dtype,table_std", [
+    (1, 32, 32, 128, 4, 16, 8, "fp16", 6.0),    # fused window 16
+    (1, 32, 32, 128, 4, 16, 0, "bf16", 40.0),   # fused window 16, every window unmasked
+    (1, 16, 24, 256, 8, 8, 4, "bf16", 80.0),    # tiled, window 8
+    (1, 32, 32, 160, 5, 16, 8, "fp16", 6.0),    # tiled, window 16
+    (1, 48, 48, 96, 3, 24, 12, "bf16", 40.0),   # tiled, window 24
+])
+def test_wmsa_large_bias(gpu, B, H, W, C, heads, M, s, dtype, table_std):
+    _say(f"large bias B={B} H={H} W={W} C={C} heads={heads} M={M} s={s} {dtype}")
+    case = workloads.make_case(B, H, W, C, heads, M, (s,), dtype, "v1", seed=7 * M + s,
+                               table_std=table_std)
+    blk = case.blocks[0]
+    y = helpers.run_gpu_block(case, blk, case.x.cuda())
+    torch.cuda.synchronize()
+    ref = helpers.run_oracle_block(case, blk, workloads.f64(case.x))
+    helpers.assert_close(workloads.f64(y.cpu()), ref, dtype, "large bias")
+
+
 def test_wmsa_empty_batch(gpu):
     case = workloads.make_case(1, 14, 14, 96, 3, 7, (3,), "bf16", "v1", seed=1)
     blk = case.blocks[0]
