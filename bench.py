@@ -25,6 +25,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import glob
 import json
 import math
@@ -179,9 +180,9 @@ class Runner:
         return {k: v / (steps * nb) for k, v in tot.items()}
 
 
-# Source file of each kernel; its digest also covers the shared headers and the
-# host-side launch code, so traffic counters taken on a kernel stay valid while
-# only other kernels change.
+# Source file of each kernel; its digest also covers the headers that file
+# includes (directly or not) and the host-side launch code, so traffic counters
+# taken on a kernel stay valid while only other kernels change.
 KERNEL_SOURCE = {
     "fused_window_kernel": "fused_window.hip", "fused_w8_kernel": "fused_w8.hip",
     "fused_w16_kernel": "fused_w16.hip", "tiled_attn_kernel": "tiled_attn.hip",
@@ -190,14 +191,29 @@ KERNEL_SOURCE = {
     "proj_tiled_kernel": "gemm_tiled.hip", "qkv_gemm_kernel": "gemm.hip",
     "proj_gemm_kernel": "gemm.hip",
 }
+_INCLUDE = re.compile(r'^\s*#\s*include\s+"([^"]+)"', re.M)
+
+
+def _source_closure(csrc, names):
+    """The named files plus every local header they include, transitively."""
+    seen, todo = set(), list(names)
+    while todo:
+        n = todo.pop()
+        p = os.path.join(csrc, n)
+        if n in seen or not os.path.exists(p):
+            continue
+        seen.add(n)
+        with open(p) as f:
+            todo.extend(_INCLUDE.findall(f.read()))
+    return sorted(os.path.join(csrc, n) for n in seen)
 
 
 def source_digest(kernel=None):
     csrc = os.path.join(ROOT, "shifted_window_attention_roll_amd", "csrc")
-    paths = sorted(glob.glob(os.path.join(csrc, "*")))
     if kernel in KERNEL_SOURCE:
-        own = KERNEL_SOURCE[kernel]
-        paths = [p for p in paths if p.endswith(".hpp") or os.path.basename(p) in (own, "api.hip")]
+        paths = _source_closure(csrc, [KERNEL_SOURCE[kernel], "api.hip"])
+    else:
+        paths = sorted(glob.glob(os.path.join(csrc, "*")))
     h = hashlib.sha256()
     for p in paths:
         with open(p, "rb") as f:

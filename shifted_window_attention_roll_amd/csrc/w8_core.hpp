@@ -16,7 +16,7 @@
 // from a ones x P^T product.
 #pragma once
 
-#include "attn_core.hpp"
+#include "kv_frag.hpp"
 
 namespace swin {
 
