@@ -49,24 +49,38 @@ namespace swin {
 // (fill_bias_table; eight 4-byte reads).
 enum class TableMode { kTable4, kTable1 };
 
-// Floats of the single reversed copy: every lane reads 8 floats from a start
-// index below (2M-1)^2.
+// The single reversed copy keeps its 2M-1 rows at a pitch of 8 x odd floats
+// (24, 40, 56 for M = 8, 16, 24): a wave's bias read touches 5 consecutive
+// rows, 8 consecutive floats each, and at that pitch they fall on distinct
+// banks (row pitch 2M-1 made them collide two ways).  Every lane reads 8
+// floats inside one row.
 template <int M>
-constexpr int table1_size() { return ((2 * M - 1) * (2 * M - 1) + 8 + 3) / 4 * 4; }
+constexpr int table1_pitch() { return ((2 * M - 1 + 7) / 8) % 2 ? (2 * M - 1 + 7) / 8 * 8 : (2 * M - 1 + 7) / 8 * 8 + 8; }
+template <int M>
+constexpr int table1_size() { return (2 * M - 1) * table1_pitch<M>(); }
 
 template <int M>
 __device__ __forceinline__ void fill_bias_table(float* rt, const float* table, int heads, int h,
                                                 int tid, int nthreads) {
-  constexpr int R = 2 * M - 1;
+  constexpr int R = 2 * M - 1, P = table1_pitch<M>();
   for (int e = tid; e < table1_size<M>(); e += nthreads) {
+    const int r = e / P, cc = e - r * P;
     float v = -__builtin_inff();
-    if (e < R * R) {
-      const int r = e / R, cc = e - r * R;
-      v = table[(int64_t)(r * R + (R - 1 - cc)) * heads + h] * kLog2e;
-    }
+    if (cc < R) v = table[(int64_t)(r * R + (R - 1 - cc)) * heads + h] * kLog2e;
     rt[e] = v;
   }
 }
+
+// Softmax reference of the unmasked windows (masked windows, and the fallback
+// of the fixed schemes, always use the lazy one):
+//   kLazy   -- moves lazily, one compare and ballot per key block;
+//   kBlock0 -- block 0's row max, fixed;
+//   kZero   -- 0, fixed (bfloat16 P only): the caller has shifted the head's
+//              bias table by a constant so that no logit (base 2) exceeds
+//              kZeroTop; no max and no subtraction at all.
+// The fixed schemes check the row sums once at the end.
+enum class RefMode { kLazy, kBlock0, kZero };
+constexpr float kZeroTop = 64.0f;
 
 struct NoHook {
   __device__ __forceinline__ void operator()(int) const {}
@@ -104,13 +118,13 @@ __device__ __forceinline__ void fill_bias_copies(float* rt4, const float* table,
 // O for the lane's query and d = 8*(l/16) + e, e = 0..7.  LAYOUT / TABLE pick
 // the K, V layout and the bias-table mode; hook(kbi) runs at the start of key
 // block kbi (the caller's work to interleave, e.g. staging the next item).
-// With FAST and !MASKED, returns false (o undefined) when the fixed-reference
-// pass saw a logit too far above its reference; the caller then runs the
+// With a fixed reference and !MASKED, returns false (o undefined) when the
+// row sums show that some P left the safe range; the caller then runs the
 // MASKED instance with my = mx = false, which is exact for any logits.
 // Otherwise returns true.
 template <typename QT, typename VT, int M, int QTL, bool MASKED,
           KvLayout LAYOUT = KvLayout::kPadded, TableMode TABLE = TableMode::kTable4,
-          bool FAST = true, class Hook = NoHook>
+          RefMode REF = RefMode::kBlock0, class Hook = NoHook>
 __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int (&tile)[QTL],
                                            const QT* ks, const VT* vs, const float* rt4,
                                            const float* ninf, int lane, int bnd, bool my, bool mx,
@@ -119,6 +133,7 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
   typedef __attribute__((address_space(3))) const f32x4* lds_f4;
   constexpr int N = M * M;
   constexpr int R = 2 * M - 1;
+  static_assert(REF != RefMode::kZero || !__is_same(VT, h16), "zero reference needs bfloat16 P");
   constexpr bool SWZ = LAYOUT == KvLayout::kSwizzled;
   constexpr bool T1 = TABLE == TableMode::kTable1;
   constexpr int LDK = SWZ ? 32 : kAttnLD;
@@ -126,6 +141,7 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
   constexpr int TPC = M / 2;  // 16-query tiles per chunk
   constexpr int BPC = M / 4;  // 32-key blocks per chunk
   constexpr int TS = table_stride<M>();
+  constexpr int P1 = table1_pitch<M>();
   const int g4 = lane >> 4, i16 = lane & 15;
   const float NEG_INF = -__builtin_inff();
   // Lazy-rescale headroom (base 2): P may reach 2^kGrow before the reference
@@ -149,13 +165,13 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     // c = 0 (the smallest), so every block adds a non-negative multiple of 4.
     // Copy (a0 % 4) of the table is shifted so that the lane's 8 floats start
     // on a 16-byte boundary.
-    const int a0 = (qy[j] - 4 * (BPC - 1) - g4 + M - 1) * R + (M - 1 - qx[j]);
+    const int a0 = (qy[j] - 4 * (BPC - 1) - g4 + M - 1) * (T1 ? P1 : R) + (M - 1 - qx[j]);
     if constexpr (T1)
       tbf[j] = (lds_f)(rt4 + a0);
     else
       tb[j] = (lds_f4)(rt4 + (a0 & 3) * TS + (a0 & ~3));
     o0[j] = o1[j] = ls[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[j] = -1e30f;
+    m[j] = (REF == RefMode::kZero && !MASKED) ? 0.0f : -1e30f;
     mt[j] = -1e30f;
   }
   vec8<VT> ones;
@@ -204,7 +220,7 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
   };
   auto load_bias = [&](int kbi, Ops& op) {
     const int ck = kbi / BPC, b = kbi - ck * BPC;
-    const int boff = 8 * ck + 4 * R * (BPC - 1 - b);
+    const int boff = 8 * ck + 4 * (T1 ? P1 : R) * (BPC - 1 - b);
 #pragma unroll
     for (int j = 0; j < QTL; ++j) {
       lds_f4 bp = tb[j] + boff / 4;
@@ -269,7 +285,8 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     }
     // Phase 1, every tile: S^T = K Q^T on top of the bias, block max (with
     // the fixed reference, only in block 0).
-    constexpr bool FIXED = FAST && !MASKED;
+    constexpr bool FIXED = REF != RefMode::kLazy && !MASKED;
+    constexpr bool BLOCK0 = FIXED && REF == RefMode::kBlock0;
     f32x4 s0[QTL], s1[QTL];
     float bm[QTL];
 #pragma unroll
@@ -288,17 +305,17 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
       }
       s0[j] = mma_16x16x32(cur.k0, qf[j], s0[j]);
       s1[j] = mma_16x16x32(cur.k1, qf[j], s1[j]);
-      if (!FIXED || kbi == 0)
+      if (!FIXED || (BLOCK0 && kbi == 0))
         bm[j] = fmaxf(fmaxf(fmaxf(s0[j][0], s0[j][1]), fmaxf(s0[j][2], s0[j][3])),
                       fmaxf(fmaxf(s1[j][0], s1[j][1]), fmaxf(s1[j][2], s1[j][3])));
     }
-    // Phase 2.  Unmasked windows with FAST: the reference is the row max of
-    // block 0 and never moves -- no per-block max, compare or branch; the
-    // row sums are checked once at the end.  Otherwise (masked windows, where
-    // a row may have no allowed key in block 0, the fallback, and !FAST)
-    // lazy: when some lane of some tile saw a logit more than kGrow above its
+    // Phase 2.  Unmasked windows with a fixed reference (block 0's row max,
+    // or 0): it never moves -- no per-block max, compare or branch; the row
+    // sums are checked once at the end.  Otherwise (masked windows, where a
+    // row may have no allowed key in block 0, the fallback, and kLazy) lazy:
+    // when some lane of some tile saw a logit more than kGrow above its
     // reference, every tile's reference moves to its row max.
-    if constexpr (FIXED) {
+    if constexpr (BLOCK0) {
       if (kbi == 0) {
 #pragma unroll
         for (int j = 0; j < QTL; ++j) m[j] = xor32_max(xor16_max(bm[j]));
@@ -338,16 +355,21 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     if (kbi + 1 < NB) cur = nxt;
   }
 
-  if constexpr (FAST && !MASKED) {
-    // Every P is at most its row sum, and the reference is at most the row
-    // max (P of the largest logit >= 1).  A row sum below kFixedLimit (also
+  if constexpr (REF != RefMode::kLazy && !MASKED) {
+    // Every P is at most its row sum.  A row sum below kFixedLimit (also
     // false for inf / NaN) means no P went past it: bfloat16 P stays far
-    // from its overflow, float16 P below 65504.  Otherwise the caller redoes
-    // the item on the lazy path.
+    // from its overflow, float16 P below 65504.  With block 0's max as the
+    // reference the largest P is >= 1; with the zero reference a row sum of
+    // at least 2^-60 keeps every P that matters a normal number.  Otherwise
+    // the caller redoes the item on the lazy path.
     constexpr float kFixedLimit = __is_same(VT, h16) ? 32768.0f : 18446744073709551616.0f;
+    constexpr float kZeroFloor = 8.673617379884035e-19f;  // 2^-60
     bool far = false;
 #pragma unroll
-    for (int j = 0; j < QTL; ++j) far = far || !(ls[j][0] < kFixedLimit);
+    for (int j = 0; j < QTL; ++j) {
+      far = far || !(ls[j][0] < kFixedLimit);
+      if constexpr (REF == RefMode::kZero) far = far || !(ls[j][0] >= kZeroFloor);
+    }
     if (__builtin_amdgcn_ballot_w64(far)) return false;
   }
   // Fragment pair t row 4*g4 + r is head dim 8*g4 + 4t + r.

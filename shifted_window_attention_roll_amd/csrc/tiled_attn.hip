@@ -22,7 +22,7 @@ namespace {
 template <int M>
 constexpr int tiled_waves_per_simd() { return M == 24 ? 3 : 4; }
 
-template <typename QT, typename VT, int M, int QTL, int WAVES>
+template <typename QT, typename VT, int M, int QTL, int WAVES, bool V2>
 __global__ __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(tiled_waves_per_simd<M>())))
 void tiled_attn_kernel(FwdParams p, int n_items) {
@@ -38,6 +38,7 @@ void tiled_attn_kernel(FwdParams p, int n_items) {
   __shared__ __attribute__((aligned(16))) VT vs[2][N * 32];
   __shared__ __attribute__((aligned(16))) float rt[table1_size<M>()];
   __shared__ __attribute__((aligned(16))) float ninf[8];
+  __shared__ float red[WAVES];  // per-wave partial maxima
 
   const Geom& g = p.g;
   int item = blockIdx.x;  // window * heads + head; the head stays fixed
@@ -69,6 +70,27 @@ void tiled_attn_kernel(FwdParams p, int n_items) {
     *reinterpret_cast<uint4*>(chunk_dst(0, c)) = gload16(chunk_src(item, c));
   fill_bias_table<M>(rt, p.table, g.heads, h, tid, NT);
   if (tid < 8) ninf[tid] = -__builtin_inff();
+  // Zero reference: cosine attention with bfloat16 P.
+  constexpr bool ZREF = V2 && !__is_same(VT, h16);
+  if constexpr (ZREF) {
+    // Cosine attention: |q . k| <= log2(e) / max(tau, tau_min) (q carries that
+    // factor, both are unit vectors; 2^-8 covers their 16-bit rounding), so
+    // every logit is at most that plus the table's largest entry.  Shifting
+    // the head's table by that bound minus kZeroTop (a constant per head
+    // leaves the softmax unchanged) lets the unmasked windows use the zero
+    // reference.
+    float bmax = -__builtin_inff();
+    for (int e = tid; e < table1_size<M>(); e += NT) bmax = fmaxf(bmax, rt[e]);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, d));
+    if (lane == 0) red[wave] = bmax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) bmax = fmaxf(bmax, red[w]);
+    const float qmult = kLog2e / fmaxf(p.tau[h], p.tau_min);
+    const float shift = qmult * (1.0f + 1.0f / 256.0f) + bmax - kZeroTop;
+    for (int e = tid; e < table1_size<M>(); e += NT) rt[e] -= shift;
+  }
 
   int tile[QTL];
 #pragma unroll
@@ -112,7 +134,8 @@ void tiled_attn_kernel(FwdParams p, int n_items) {
     float o[QTL][8];
     bool done = false;
     if (!(my || mx))
-      done = attn_tiles<QT, VT, M, QTL, false, KvLayout::kSwizzled, TableMode::kTable1>(
+      done = attn_tiles<QT, VT, M, QTL, false, KvLayout::kSwizzled, TableMode::kTable1,
+                        ZREF ? RefMode::kZero : RefMode::kBlock0>(
           qf, tile, ks[buf], vs[buf], rt, ninf, lane, M - g.s, false, false, o, hook);
     if (!done)
       attn_tiles<QT, VT, M, QTL, true, KvLayout::kSwizzled, TableMode::kTable1>(
@@ -148,8 +171,12 @@ hipError_t tiled_launch(const FwdParams& p, int per_cu, hipStream_t st) {
   if (grid > n) grid = n;
   grid = grid / p.g.heads * p.g.heads;
   if (grid < p.g.heads) grid = p.g.heads;
-  hipLaunchKernelGGL((tiled_attn_kernel<QT, VT, M, QTL, WAVES>), dim3(grid), dim3(64 * WAVES), 0, st,
-                     p, n);
+  if (p.v2)
+    hipLaunchKernelGGL((tiled_attn_kernel<QT, VT, M, QTL, WAVES, true>), dim3(grid),
+                       dim3(64 * WAVES), 0, st, p, n);
+  else
+    hipLaunchKernelGGL((tiled_attn_kernel<QT, VT, M, QTL, WAVES, false>), dim3(grid),
+                       dim3(64 * WAVES), 0, st, p, n);
   return hipGetLastError();
 }
 

@@ -151,6 +151,37 @@ def test_wmsa_large_bias(gpu, B, H, W, C, heads, M, s, dtype, table_std):
     helpers.assert_close(workloads.f64(y.cpu()), ref, dtype, "large bias")
 
 
+# Cosine attention with one relative-position entry raised far above the rest:
+# the shifted-table (zero) reference of the tiled kernel sees its other rows'
+# exponentials underflow and hands over to the exact lazy pass; the block-0
+# reference of the window-16 kernel sees the spike's row sums overflow.
+@pytest.mark.parametrize("B,H,W,C,heads,M,s", [
+    (1, 24, 48, 160, 5, 8, 0),     # tiled, window 8, every window unmasked
+    (1, 32, 32, 160, 5, 16, 8),    # tiled, window 16
+    (1, 48, 48, 96, 3, 24, 12),    # tiled, window 24
+    (1, 32, 32, 128, 4, 16, 0),    # fused window 16
+])
+def test_wmsa_v2_table_spike(gpu, B, H, W, C, heads, M, s):
+    _say(f"v2 table spike B={B} H={H} W={W} C={C} heads={heads} M={M} s={s}")
+    import shifted_window_attention_roll_amd as swin
+    case = workloads.make_case(B, H, W, C, heads, M, (s,), "bf16", "v2", seed=3 * M + s,
+                               tau="uniform")
+    blk = case.blocks[0]
+    table = helpers.oracle_table(case, blk).copy()
+    R = 2 * M - 1
+    table[(R * R) // 2 + 1, :] += 150.0  # one (dy, dx) pair per row at most
+    dev = "cuda"
+    y = swin.wmsa_fwd(case.x.to(dev), blk.w_qkv.to(dev), blk.b_qkv.to(dev), blk.w_proj.to(dev),
+                      blk.b_proj.to(dev), torch.from_numpy(table).float().to(dev), M, s, heads,
+                      "v2", tau=blk.tau.to(dev))
+    torch.cuda.synchronize()
+    ref = so.wmsa_forward(workloads.f64(case.x), workloads.f64(blk.w_qkv),
+                          workloads.f64(blk.b_qkv), workloads.f64(blk.w_proj),
+                          workloads.f64(blk.b_proj), table.astype(np.float32).astype(np.float64),
+                          M, s, heads, "v2", tau=workloads.f64(blk.tau))
+    helpers.assert_close(workloads.f64(y.cpu()), ref, "bf16", "v2 table spike")
+
+
 def test_wmsa_empty_batch(gpu):
     case = workloads.make_case(1, 14, 14, 96, 3, 7, (3,), "bf16", "v1", seed=1)
     blk = case.blocks[0]
