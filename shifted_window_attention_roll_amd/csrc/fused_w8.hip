@@ -250,9 +250,12 @@ void fused_w8_kernel(FwdParams p, int n_windows) {
     T* os = reinterpret_cast<T*>(ks[h]) + i16 * LDK + 8 * g4;
     auto store_o = [&](int j, const vec8<T>& of) { store8(os + 16 * j * LDK, of); };
     if (my || mx)
-      w8_attend<QT, T, MV, true>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, my, mx, store_o);
-    else
-      w8_attend<QT, T, MV, false>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, false, false, store_o);
+      w8_attend<QT, T, MV, true, false>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, my, mx, store_o);
+    else if (!w8_attend<QT, T, MV, false, true>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, false,
+                                                  false, store_o))
+      // Some row outgrew the zero reference: redo with exact row maxima.
+      w8_attend<QT, T, MV, false, false>(qf, kf, vf, tb0, tb1, qy0, qx, g4, bnd, false, false,
+                                           store_o);
     // The next window's token rows, in flight across the barrier and the
     // projection.
     int cur[4];

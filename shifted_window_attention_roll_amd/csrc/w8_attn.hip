@@ -119,9 +119,10 @@ void w8_attn_kernel(FwdParams p, int n_items) {
         gstore16(og + (int64_t)((2 * j + qy0) * MV + qx) * g.C, __builtin_bit_cast(uint4, of));
     };
     if (my || mx)
-      w8_attend<QT, VT, MV, true>(qc, kf, vf, tb0, tb1, qy0, qx, g4, bnd, my, mx, store_o);
-    else
-      w8_attend<QT, VT, MV, false>(qc, kf, vf, tb0, tb1, qy0, qx, g4, bnd, false, false, store_o);
+      w8_attend<QT, VT, MV, true, false>(qc, kf, vf, tb0, tb1, qy0, qx, g4, bnd, my, mx, store_o);
+    else  // exact row maxima: a zero-reference pass would need more registers here
+      w8_attend<QT, VT, MV, false, false>(qc, kf, vf, tb0, tb1, qy0, qx, g4, bnd, false, false,
+                                          store_o);
     // The next item's K / V stores must not pass this item's fragment reads.
     asm volatile("" ::: "memory");
   }

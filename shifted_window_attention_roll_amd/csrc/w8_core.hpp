@@ -29,8 +29,12 @@ constexpr int kTab = kTabRows + kPadInf;
 
 typedef __attribute__((address_space(3))) const float* lds_f;
 
-template <typename QT, typename T, int MV, bool MASKED, class Store>
-__device__ __forceinline__ void w8_attend(const vec8<QT> (&qf)[4], const vec8<QT> (&kf)[2][2],
+// ZERO: the softmax reference is 0 instead of the exact row max (no max
+// reductions); returns false when some real query's row sum left the safe
+// range (every tile has been stored all the same), and the caller then redoes
+// the item with ZERO = false, which overwrites every store and returns true.
+template <typename QT, typename T, int MV, bool MASKED, bool ZERO, class Store>
+__device__ __forceinline__ bool w8_attend(const vec8<QT> (&qf)[4], const vec8<QT> (&kf)[2][2],
                                           const vec8<T> (&vf)[2][2], lds_f tb0,
                                           lds_f tb1, int qy0, int qx, int g4, int bnd,
                                           bool my, bool mx, Store store) {
@@ -44,6 +48,14 @@ __device__ __forceinline__ void w8_attend(const vec8<QT> (&qf)[4], const vec8<QT
     const unsigned lm = (1u << bnd) - 1u;
     xbits = qx < bnd ? lm : (~lm & 0xffu);
   }
+  // Safe range of a row sum with the zero reference: float16 P below 2^15
+  // (its largest finite value is 65504) and a row sum of at least 1 (the
+  // largest P >= 1/64, so P too small for a normal float16 hardly matters);
+  // bfloat16 P between 2^-60 and 2^64.
+  constexpr bool H16 = __is_same(T, h16);
+  constexpr float kLo = H16 ? 1.0f : 8.673617379884035e-19f;
+  constexpr float kHi = H16 ? 32768.0f : 18446744073709551616.0f;
+  bool bad = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     // Logits of the lane's query (slot 16j + l%16) against keys 32b + 8g + e:
@@ -76,14 +88,17 @@ __device__ __forceinline__ void w8_attend(const vec8<QT> (&qf)[4], const vec8<QT
 #pragma unroll
       for (int t = 0; t < 2; ++t) s[b][t] = mma_16x16x32(kf[b][t], qf[j], s[b][t]);
     // Exact row max over the 64 keys (column 7 is padding for side 7).
-    float m = NEG_INF;
+    float m = 0.f;
+    if constexpr (!ZERO) {
+      m = NEG_INF;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < MV) m = fmaxf(m, s[b][e >> 2][e & 3]);
-    m = xor32_max(xor16_max(m));
-    if constexpr (MASKED) m = m == NEG_INF ? 0.f : m;  // padded query with no allowed key
+        for (int e = 0; e < 8; ++e)
+          if (e < MV) m = fmaxf(m, s[b][e >> 2][e & 3]);
+      m = xor32_max(xor16_max(m));
+      if constexpr (MASKED) m = m == NEG_INF ? 0.f : m;  // padded query with no allowed key
+    }
     f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0, l = o0;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -95,6 +110,8 @@ __device__ __forceinline__ void w8_attend(const vec8<QT> (&qf)[4], const vec8<QT
       o1 = mma_16x16x32(vf[b][1], pf, o1);
       l = mma_16x16x32(ones, pf, l);
     }
+    // Only the window's real queries count (padding slots are not stored).
+    if constexpr (ZERO) bad = bad || (2 * j + qy0 < MV && qx < MV && !(l[0] >= kLo && l[0] < kHi));
     const float inv = __builtin_amdgcn_rcpf(l[0]);
     vec8<T> of;
 #pragma unroll
@@ -105,6 +122,7 @@ __device__ __forceinline__ void w8_attend(const vec8<QT> (&qf)[4], const vec8<QT
     // O of the lane's query (slot 16j + l%16), dims 8g .. 8g+7.
     store(j, of);
   }
+  return !(ZERO && __builtin_amdgcn_ballot_w64(bad));
 }
 
 

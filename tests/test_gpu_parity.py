@@ -130,15 +130,19 @@ def test_wmsa_small(gpu, B, H, W, C, heads, M, s, dtype, mode, bias_std):
 
 
 # Relative-position biases far larger than the logits' usual spread: rows
-# whose largest logit lies well past their first key block's, so the
-# attention core's fixed-reference pass hands over to its exact lazy pass
-# (kGrow = 8 in base 2 with float16 P, 64 with bfloat16 P).
+# whose largest logit lies well past their first key block's (or far from 0),
+# so the attention cores' fixed-reference passes hand over to their exact
+# passes (lazy reference for windows 8 - 24, exact row max for windows 7 / 8).
 @pytest.mark.parametrize("B,H,W,C,heads,M,s,dtype,table_std", [
     (1, 32, 32, 128, 4, 16, 8, "fp16", 6.0),    # fused window 16
     (1, 32, 32, 128, 4, 16, 0, "bf16", 40.0),   # fused window 16, every window unmasked
     (1, 16, 24, 256, 8, 8, 4, "bf16", 80.0),    # tiled, window 8
     (1, 32, 32, 160, 5, 16, 8, "fp16", 6.0),    # tiled, window 16
     (1, 48, 48, 96, 3, 24, 12, "bf16", 40.0),   # tiled, window 24
+    (2, 14, 14, 96, 3, 7, 3, "fp16", 6.0),      # fused window 7
+    (1, 16, 16, 64, 2, 8, 4, "bf16", 80.0),     # fused window 8
+    (1, 14, 21, 192, 6, 7, 3, "bf16", 80.0),    # window 7 between the GEMMs
+    (1, 21, 14, 160, 5, 7, 0, "fp16", 6.0),     # window 7 between the GEMMs, no shift
 ])
 def test_wmsa_large_bias(gpu, B, H, W, C, heads, M, s, dtype, table_std):
     _say(f"large bias B={B} H={H} W={W} C={C} heads={heads} M={M} s={s} {dtype}")
