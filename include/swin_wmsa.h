@@ -167,6 +167,50 @@ swin_status swin_wmsa_fwd_timed(const swin_wmsa_desc* desc, const void* x, const
                                 void* workspace, size_t ws_bytes, void* stream,
                                 void* const* events, int n_events);
 
+/*
+ * Full block forward around the attention sub-layer.
+ *   Pages: "Boost Vision Transformer with GPU-Friendly Sparsity and
+ *   Quantization" -- Section 3.2 / Figure 3 (the Swin block is the standard
+ *   transformer block with shifted-window attention in place of multi-head
+ *   attention; the feed-forward layers are GEMMs) and Section 2.2 (GeLU);
+ *   "Boosting Swin Transformer Speed", Training Optimization (LayerNorm in the
+ *   block); "Swin Transformer V2" summary, How It Works (V1 pre-norm, V2
+ *   residual post-norm).
+ *   V1 (attn.mode == SWIN_V1):  h = x + A(LN1(x)),  y = h + F(LN2(h))
+ *   V2 (attn.mode == SWIN_V2):  h = x + LN1(A(x)),  y = h + LN2(F(h))
+ *   A = swin_wmsa_fwd with `attn` and the attention parameters below;
+ *   LN(v) = (v - mean) / sqrt(var + ln_eps) * gamma + beta over the C channels
+ *   of a token (biased variance); F(u) = GELU(u fc1_w^T + fc1_b) fc2_w^T + fc2_b
+ *   with the exact GELU v * Phi(v).
+ * Parameters (device pointers, attn.dtype unless noted): the attention's as in
+ * swin_wmsa_fwd; ln1_g, ln1_b, ln2_g, ln2_b [C]; fc1_w [hidden, C], fc1_b
+ * [hidden] or NULL; fc2_w [C, hidden], fc2_b [C] or NULL.
+ *   x, y [B, H, W, C]; y must not overlap x or the workspace.
+ *   workspace, ws_bytes >= swin_block_workspace_size(desc): the attention's
+ *   workspace plus four intermediates (three [B*H*W, C], one [B*H*W, hidden]).
+ * Requires a valid attention descriptor, hidden a multiple of 32 (<= 16384),
+ * C <= 512 (else SWIN_ERR_UNSUPPORTED); LayerNorms and GELU in float32; the
+ * intermediates are stored in attn.dtype.
+ */
+typedef struct {
+  swin_wmsa_desc attn;
+  int hidden;     /* MLP hidden width (4C in the usual block)                  */
+  float ln_eps;   /* LayerNorm epsilon; <= 0 selects 1e-5                      */
+} swin_block_desc;
+
+typedef struct {
+  const void *w_qkv, *b_qkv, *w_proj, *b_proj;
+  const float *bias_table, *tau;
+  const void *ln1_g, *ln1_b, *ln2_g, *ln2_b;
+  const void *fc1_w, *fc1_b, *fc2_w, *fc2_b;
+} swin_block_params;
+
+/* Workspace bytes of swin_block_fwd (0 for an invalid descriptor or B == 0). */
+size_t swin_block_workspace_size(const swin_block_desc* d);
+
+swin_status swin_block_fwd(const swin_block_desc* d, const void* x, const swin_block_params* p,
+                           void* y, void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ SWIN_V1, SWIN_V2 = 1, 2
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _EXPORTS = ("swin_status_str", "swin_abi_version", "swin_partition_shift", "swin_reverse_unshift",
             "swin_cpb_table", "swin_wmsa_workspace_size", "swin_wmsa_fwd",
-            "swin_wmsa_kernel_count", "swin_wmsa_kernel_name", "swin_wmsa_fwd_timed")
+            "swin_wmsa_kernel_count", "swin_wmsa_kernel_name", "swin_wmsa_fwd_timed",
+            "swin_block_workspace_size", "swin_block_fwd")
 
 
 class SwinDesc(ctypes.Structure):
@@ -29,6 +30,16 @@ class SwinDesc(ctypes.Structure):
                 ("C", ctypes.c_int), ("heads", ctypes.c_int), ("M", ctypes.c_int),
                 ("s", ctypes.c_int), ("mode", ctypes.c_int), ("dtype", ctypes.c_int),
                 ("scale", ctypes.c_float), ("tau_min", ctypes.c_float)]
+
+
+class BlockDesc(ctypes.Structure):
+    _fields_ = [("attn", SwinDesc), ("hidden", ctypes.c_int), ("ln_eps", ctypes.c_float)]
+
+
+class BlockParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_qkv", "b_qkv", "w_proj", "b_proj", "bias_table", "tau", "ln1_g", "ln1_b",
+                 "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
 
 
 _lib = None
@@ -66,6 +77,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swin_wmsa_kernel_count.argtypes = [ctypes.POINTER(SwinDesc)]
     lib.swin_wmsa_kernel_name.restype = ctypes.c_char_p
     lib.swin_wmsa_kernel_name.argtypes = [ctypes.POINTER(SwinDesc), i]
+    lib.swin_block_workspace_size.restype = ctypes.c_size_t
+    lib.swin_block_workspace_size.argtypes = [ctypes.POINTER(BlockDesc)]
+    lib.swin_block_fwd.restype = st
+    lib.swin_block_fwd.argtypes = [ctypes.POINTER(BlockDesc), vp, ctypes.POINTER(BlockParams), vp,
+                                   vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -176,5 +192,41 @@ def wmsa_fwd(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv: Optional[torch.Tensor]
     return out
 
 
+def make_block_desc(B, H, W, C, heads, M, s, mode="v1", dtype=torch.bfloat16, hidden=None,
+                    scale=0.0, tau_min=0.0, ln_eps=0.0) -> BlockDesc:
+    return BlockDesc(make_desc(B, H, W, C, heads, M, s, mode, dtype, scale, tau_min),
+                     int(4 * C if hidden is None else hidden), float(ln_eps))
+
+
+def block_workspace_size(desc: BlockDesc) -> int:
+    return int(load_library().swin_block_workspace_size(ctypes.byref(desc)))
+
+
+_BLOCK_KEYS = ("w_qkv", "b_qkv", "w_proj", "b_proj", "table", "tau", "ln1_g", "ln1_b", "ln2_g",
+               "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
+
+
+def block_fwd(x: torch.Tensor, params: dict, M: int, s: int, heads: int, mode: str = "v1",
+              scale: float = 0.0, tau_min: float = 0.0, ln_eps: float = 0.0,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """Full block forward (LayerNorms, attention, MLP, residuals; V1 pre-norm or
+    V2 post-norm); ``params`` maps the names of ``swin_block_params`` (``table``
+    for the bias table) to device tensors, biases may be absent."""
+    B, H, W, C = x.shape
+    desc = make_block_desc(B, H, W, C, heads, M, s, mode, x.dtype, params["fc1_w"].shape[0],
+                           scale, tau_min, ln_eps)
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = torch.empty(max(block_workspace_size(desc), 1), dtype=torch.uint8,
+                                device=x.device)
+    bp = BlockParams(*[_ptr(params.get(k)) for k in _BLOCK_KEYS])
+    _check(load_library().swin_block_fwd(ctypes.byref(desc), _ptr(x), ctypes.byref(bp), _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
 __all__ = ["load_library", "make_desc", "workspace_size", "partition_shift", "reverse_unshift",
-           "cpb_table", "wmsa_fwd", "kernel_names", "SwinDesc", "SwinError", "LIB_PATH"]
+           "cpb_table", "wmsa_fwd", "kernel_names", "SwinDesc", "SwinError", "LIB_PATH",
+           "BlockDesc", "BlockParams", "make_block_desc", "block_workspace_size", "block_fwd"]

@@ -1,0 +1,269 @@
+// Full Swin block forward around the attention sub-layer: the two LayerNorms,
+// the MLP (Linear + GELU, Linear) and the residual connections, in the V1
+// pre-norm and the V2 post-norm arrangement.
+//
+// Pages: "Boost Vision Transformer with GPU-Friendly Sparsity and Quantization",
+// Section 3.2 / Figure 3 (the Swin block is the standard transformer block with
+// shifted-window attention in place of multi-head attention; the feed-forward
+// layers are GEMMs) and Section 2.2 (GeLU as the activation); "Boosting Swin
+// Transformer Speed", Training Optimization (LayerNorm is part of the block);
+// "Swin Transformer V2" summary, How It Works (V1 normalises before each
+// sub-layer, V2 normalises each residual branch before adding it back).
+//
+//   V1:  h = x + A(LN1(x)),   y = h + F(LN2(h))
+//   V2:  h = x + LN1(A(x)),   y = h + LN2(F(h))
+// with A = swin_wmsa_fwd and F(u) = GELU(u W1^T + b1) W2^T + b2 (exact GELU).
+//
+// Kernels: ln_kernel (one wave per token; the residual adds are fused into it
+// or into the second GEMM) and dense_kernel (the general matrix-core tile of
+// gemm_core.hpp with a bias / GELU / residual epilogue).
+#include <string.h>
+
+#include "gemm_core.hpp"
+#include "swin_wmsa.h"
+
+namespace swin {
+
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
+constexpr int kLnMaxPerLane = 8;  // C <= 512
+
+// v = a (+ b); u (if given) <- v; out <- LN(v) * gamma + beta (+ r).  LayerNorm
+// over the C channels of a token, biased variance, in float32.  One wave per
+// token row, four rows per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void ln_kernel(const T* __restrict__ a, const T* __restrict__ b,
+                                                 T* __restrict__ u, const T* __restrict__ gamma,
+                                                 const T* __restrict__ beta,
+                                                 const T* __restrict__ r, T* __restrict__ out,
+                                                 int rows, int C, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t base = (int64_t)row * C;
+  float v[kLnMaxPerLane];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxPerLane; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = 0.f;
+    if (c < C) {
+      v[i] = (float)a[base + c] + (b ? (float)b[base + c] : 0.f);
+      s += v[i];
+    }
+  }
+  const float mean = wave_sum(s) / (float)C;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnMaxPerLane; ++i) {
+    const int c = lane + 64 * i;
+    if (c < C) q += (v[i] - mean) * (v[i] - mean);
+  }
+  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)C + eps);
+#pragma unroll
+  for (int i = 0; i < kLnMaxPerLane; ++i) {
+    const int c = lane + 64 * i;
+    if (c >= C) continue;
+    if (u) u[base + c] = (T)v[i];
+    float z = (v[i] - mean) * rstd * (float)gamma[c] + (float)beta[c];
+    if (r) z += (float)r[base + c];
+    out[base + c] = (T)z;
+  }
+}
+
+// Y = act(A Wt^T + bias) (+ R): A [rows, K], Wt [N, K] (nn.Linear layout), bias
+// [N] or null, R / Y [rows, N].  Workgroup tile 128 x BN (gemm_core.hpp); lane l
+// of wave w holds column (l % 16) of rows 32w + 16i + 4(l/16) + r.
+template <typename T, int BN, bool GELU, bool RES>
+__global__ __launch_bounds__(kThreads) void dense_kernel(const T* __restrict__ A,
+                                                         const T* __restrict__ Wt,
+                                                         const T* __restrict__ bias,
+                                                         const T* __restrict__ R,
+                                                         T* __restrict__ Y, int rows, int N, int K) {
+  __shared__ GemmSmem<T, BN> sm;
+  const int m0 = blockIdx.x * kBM, n0 = blockIdx.y * BN;
+  f32x4 acc[2][BN / 16];
+  gemm_tile<T, BN, false>(A, Geom{}, rows, m0, Wt, n0, K, sm, acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < BN / 16; ++j) {
+    const int col = n0 + j * 16 + (lane & 15);
+    const float bj = bias ? (float)bias[col] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wave * 32 + i * 16 + (lane >> 4) * 4 + r;
+        if (row >= rows) continue;
+        float v = acc[i][j][r] + bj;
+        // GELU(v) = v * Phi(v) = v (1 + erf(v / sqrt 2)) / 2.
+        if constexpr (GELU) v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+        const int64_t o = (int64_t)row * N + col;
+        if constexpr (RES) v += (float)R[o];
+        Y[o] = (T)v;
+      }
+  }
+}
+
+template <typename T>
+hipError_t launch_ln(const T* a, const T* b, T* u, const T* g, const T* be, const T* r, T* out,
+                     int rows, int C, float eps, hipStream_t st) {
+  hipLaunchKernelGGL((ln_kernel<T>), dim3((rows + 3) / 4), dim3(256), 0, st, a, b, u, g, be, r,
+                     out, rows, C, eps);
+  return hipGetLastError();
+}
+
+template <typename T, bool GELU, bool RES>
+hipError_t launch_dense(const T* A, const T* Wt, const T* bias, const T* R, T* Y, int rows, int N,
+                        int K, hipStream_t st) {
+  const int gx = (rows + kBM - 1) / kBM;
+  if (N % 128 == 0)
+    hipLaunchKernelGGL((dense_kernel<T, 128, GELU, RES>), dim3(gx, N / 128), dim3(kThreads), 0,
+                       st, A, Wt, bias, R, Y, rows, N, K);
+  else if (N % 96 == 0)
+    hipLaunchKernelGGL((dense_kernel<T, 96, GELU, RES>), dim3(gx, N / 96), dim3(kThreads), 0, st,
+                       A, Wt, bias, R, Y, rows, N, K);
+  else if (N % 64 == 0)
+    hipLaunchKernelGGL((dense_kernel<T, 64, GELU, RES>), dim3(gx, N / 64), dim3(kThreads), 0, st,
+                       A, Wt, bias, R, Y, rows, N, K);
+  else
+    hipLaunchKernelGGL((dense_kernel<T, 32, GELU, RES>), dim3(gx, N / 32), dim3(kThreads), 0, st,
+                       A, Wt, bias, R, Y, rows, N, K);
+  return hipGetLastError();
+}
+
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+struct BlockLayout {
+  size_t attn, a, b, h, u, total;
+};
+
+BlockLayout block_layout(const swin_block_desc* d) {
+  const swin_wmsa_desc& at = d->attn;
+  const size_t e = at.dtype == SWIN_F32 ? 4 : 2;
+  const size_t T = (size_t)at.B * at.H * at.W;
+  BlockLayout L;
+  L.attn = 0;
+  L.a = round256(swin_wmsa_workspace_size(&at));
+  L.b = L.a + round256(T * at.C * e);
+  L.h = L.b + round256(T * at.C * e);
+  L.u = L.h + round256(T * at.C * e);
+  L.total = L.u + round256(T * (size_t)d->hidden * e);
+  return L;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+swin_status hip_status(hipError_t e) { return e == hipSuccess ? SWIN_OK : SWIN_ERR_HIP; }
+
+template <typename T>
+swin_status block_run(const swin_block_desc* d, const T* x, const swin_block_params* p, T* y,
+                      char* ws, size_t ws_bytes, hipStream_t st) {
+  const swin_wmsa_desc& at = d->attn;
+  const BlockLayout L = block_layout(d);
+  const int rows = at.B * at.H * at.W, C = at.C, hid = d->hidden;
+  const float eps = d->ln_eps > 0.f ? d->ln_eps : 1e-5f;
+  T* A = reinterpret_cast<T*>(ws + L.a);
+  T* Bv = reinterpret_cast<T*>(ws + L.b);
+  T* Hb = reinterpret_cast<T*>(ws + L.h);
+  T* U = reinterpret_cast<T*>(ws + L.u);
+  auto P = [](const void* q) { return static_cast<const T*>(q); };
+  const size_t attn_ws = L.a;  // the attention's workspace is the first region
+  swin_status s;
+  hipError_t e;
+  if (at.mode == SWIN_V1) {
+    e = launch_ln<T>(x, nullptr, nullptr, P(p->ln1_g), P(p->ln1_b), nullptr, A, rows, C, eps, st);
+    if (e != hipSuccess) return hip_status(e);
+    s = swin_wmsa_fwd(&at, A, p->w_qkv, p->b_qkv, p->w_proj, p->b_proj, p->bias_table, p->tau, Bv,
+                      attn_ws ? ws : nullptr, attn_ws, st);
+    if (s != SWIN_OK) return s;
+    e = launch_ln<T>(x, Bv, Hb, P(p->ln2_g), P(p->ln2_b), nullptr, A, rows, C, eps, st);
+    if (e == hipSuccess)
+      e = launch_dense<T, true, false>(A, P(p->fc1_w), P(p->fc1_b), nullptr, U, rows, hid, C, st);
+    if (e == hipSuccess)
+      e = launch_dense<T, false, true>(U, P(p->fc2_w), P(p->fc2_b), Hb, y, rows, C, hid, st);
+    return hip_status(e);
+  }
+  s = swin_wmsa_fwd(&at, x, p->w_qkv, p->b_qkv, p->w_proj, p->b_proj, p->bias_table, p->tau, Bv,
+                    attn_ws ? ws : nullptr, attn_ws, st);
+  if (s != SWIN_OK) return s;
+  e = launch_ln<T>(Bv, nullptr, nullptr, P(p->ln1_g), P(p->ln1_b), x, Hb, rows, C, eps, st);
+  if (e == hipSuccess)
+    e = launch_dense<T, true, false>(Hb, P(p->fc1_w), P(p->fc1_b), nullptr, U, rows, hid, C, st);
+  if (e == hipSuccess)
+    e = launch_dense<T, false, false>(U, P(p->fc2_w), P(p->fc2_b), nullptr, A, rows, C, hid, st);
+  if (e == hipSuccess)
+    e = launch_ln<T>(A, nullptr, nullptr, P(p->ln2_g), P(p->ln2_b), Hb, y, rows, C, eps, st);
+  (void)ws_bytes;
+  return hip_status(e);
+}
+
+}  // namespace
+
+}  // namespace swin
+
+extern "C" {
+
+size_t swin_block_workspace_size(const swin_block_desc* d) {
+  if (!d || swin_wmsa_kernel_count(&d->attn) == 0) return 0;
+  if (d->hidden < 32 || d->hidden % 32) return 0;
+  return swin::block_layout(d).total;
+}
+
+swin_status swin_block_fwd(const swin_block_desc* d, const void* x, const swin_block_params* p,
+                           void* y, void* workspace, size_t ws_bytes, void* stream) {
+  using namespace swin;
+  if (!d || !p) return SWIN_ERR_NULL;
+  const swin_wmsa_desc& at = d->attn;
+  if (at.B < 0) return SWIN_ERR_SHAPE;
+  if (at.B == 0) return SWIN_OK;
+  if (swin_wmsa_kernel_count(&at) == 0) return SWIN_ERR_SHAPE;  // invalid attention desc
+  if (d->hidden < 32 || d->hidden % 32 || d->hidden > 16384) return SWIN_ERR_SHAPE;
+  if (at.C > 64 * kLnMaxPerLane) return SWIN_ERR_UNSUPPORTED;
+  if (!x || !y || !workspace || !p->w_qkv || !p->w_proj || !p->bias_table || !p->ln1_g ||
+      !p->ln1_b || !p->ln2_g || !p->ln2_b || !p->fc1_w || !p->fc2_w)
+    return SWIN_ERR_NULL;
+  if (at.mode == SWIN_V2 && !p->tau) return SWIN_ERR_NULL;
+  const BlockLayout L = block_layout(d);
+  if (ws_bytes < L.total) return SWIN_ERR_WORKSPACE;
+  const size_t e = at.dtype == SWIN_F32 ? 4 : 2;
+  const size_t act = (size_t)at.B * at.H * at.W * at.C * e;
+  const size_t C = at.C, hid = d->hidden;
+  if (overlaps(y, act, x, act) || overlaps(y, act, workspace, L.total) ||
+      overlaps(workspace, L.total, x, act) || overlaps(y, act, p->fc1_w, hid * C * e) ||
+      overlaps(y, act, p->fc2_w, hid * C * e) || overlaps(workspace, L.total, p->fc1_w, hid * C * e) ||
+      overlaps(workspace, L.total, p->fc2_w, hid * C * e))
+    return SWIN_ERR_ALIAS;
+  if (!al16(x) || !al16(y) || !al16(workspace) || !al16(p->fc1_w) || !al16(p->fc2_w) ||
+      !al16(p->w_qkv) || !al16(p->w_proj))
+    return SWIN_ERR_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  switch (at.dtype) {
+    case SWIN_F32:
+      return block_run<float>(d, static_cast<const float*>(x), p, static_cast<float*>(y), ws,
+                              ws_bytes, st);
+    case SWIN_F16:
+      return block_run<h16>(d, static_cast<const h16*>(x), p, static_cast<h16*>(y), ws, ws_bytes,
+                            st);
+    case SWIN_BF16:
+      return block_run<b16>(d, static_cast<const b16*>(x), p, static_cast<b16*>(y), ws, ws_bytes,
+                            st);
+    default:
+      return SWIN_ERR_DTYPE;
+  }
+}
+
+}  // extern "C"

@@ -166,3 +166,43 @@ def test_kernel_names_and_timed_rejects(lib):
     assert lib.swin_wmsa_fwd_timed(*args, ev, 3) == SHAPE
     ev_null = (ctypes.c_void_p * 4)(FAKE * 64, None, FAKE * 66, FAKE * 67)
     assert lib.swin_wmsa_fwd_timed(*args, ev_null, 4) == NULL
+
+
+def _block(lib, d, x=FAKE, y=FAKE * 8, ws=FAKE * 64, ws_bytes=None, **over):
+    if ws_bytes is None:
+        ws_bytes = lib.swin_block_workspace_size(ctypes.byref(d))
+    names = [f[0] for f in swin.BlockParams._fields_]
+    vals = {n: FAKE * (100 + i) for i, n in enumerate(names)}
+    vals.update(over)
+    bp = swin.BlockParams(*[vals[n] for n in names])
+    return lib.swin_block_fwd(ctypes.byref(d), x, ctypes.byref(bp), y, ws, ws_bytes, None)
+
+
+def test_block_workspace_size(lib):
+    d = swin.make_block_desc(2, 56, 56, 96, 3, 7, 3, "v1", torch.float16)
+    T = 2 * 56 * 56
+    # three [T, C] intermediates and one [T, 4C], 16-bit (the attention needs none here)
+    assert lib.swin_block_workspace_size(ctypes.byref(d)) >= 3 * T * 96 * 2 + T * 384 * 2
+    d2 = swin.make_block_desc(2, 64, 64, 160, 5, 16, 8, "v1", torch.bfloat16)
+    assert lib.swin_block_workspace_size(ctypes.byref(d2)) >= \
+        swin.workspace_size(d2.attn) + 3 * 2 * 64 * 64 * 160 * 2
+    assert lib.swin_block_workspace_size(ctypes.byref(
+        swin.make_block_desc(2, 50, 56, 96, 3, 7, 3))) == 0                   # H % M
+    assert lib.swin_block_workspace_size(ctypes.byref(
+        swin.make_block_desc(2, 56, 56, 96, 3, 7, 3, hidden=100))) == 0       # hidden % 32
+
+
+def test_block_rejects_before_launch(lib):
+    d = swin.make_block_desc(2, 56, 56, 96, 3, 7, 3, "v1", torch.float16)
+    assert _block(lib, swin.make_block_desc(0, 56, 56, 96, 3, 7, 3)) == OK    # empty batch
+    assert _block(lib, swin.make_block_desc(2, 50, 56, 96, 3, 7, 3)) == SHAPE
+    assert _block(lib, swin.make_block_desc(2, 56, 56, 96, 3, 7, 3, hidden=48)) == SHAPE
+    assert _block(lib, swin.make_block_desc(1, 14, 14, 1024, 32, 7, 3)) == UNSUP  # C > 512
+    assert _block(lib, d, x=None) == NULL
+    assert _block(lib, d, ln2_g=None) == NULL
+    assert _block(lib, d, fc1_w=None) == NULL
+    assert _block(lib, swin.make_block_desc(2, 56, 56, 96, 3, 7, 3, "v2"), tau=None) == NULL
+    assert _block(lib, d, ws_bytes=64) == WS
+    assert _block(lib, d, y=FAKE + 64) == ALIAS                              # y overlaps x
+    assert _block(lib, d, x=FAKE + 8) == ALIGN
+    assert lib.swin_block_fwd(None, FAKE, None, FAKE, FAKE, 0, None) == NULL

@@ -145,6 +145,27 @@ def make_case(B: int, H: int, W: int, C: int, heads: int, M: int,
                 blocks=blocks)
 
 
+def make_block_params(C: int, dtype: str, seed: int, hidden: Optional[int] = None,
+                      fc_std: float = 0.1, ln_std: float = 0.1) -> Dict[str, torch.Tensor]:
+    """Seeded parameters of the rest of a full block (the LayerNorms and the MLP),
+    rounded to ``dtype``: ln*_g ~ N(1, ln_std), ln*_b ~ N(0, ln_std), fc1 [hidden, C]
+    and fc2 [C, hidden] ~ N(0, fc_std), their biases ~ N(0, fc_std / 2); hidden
+    defaults to 4C."""
+    hidden = 4 * C if hidden is None else hidden
+    g = [np.random.Generator(np.random.PCG64(c))
+         for c in np.random.SeedSequence(seed).spawn(8)]
+    return {
+        "ln1_g": _to(1.0 + _normal(g[0], (C,), ln_std), dtype),
+        "ln1_b": _to(_normal(g[1], (C,), ln_std), dtype),
+        "ln2_g": _to(1.0 + _normal(g[2], (C,), ln_std), dtype),
+        "ln2_b": _to(_normal(g[3], (C,), ln_std), dtype),
+        "fc1_w": _to(_normal(g[4], (hidden, C), fc_std), dtype),
+        "fc1_b": _to(_normal(g[5], (hidden,), fc_std / 2), dtype),
+        "fc2_w": _to(_normal(g[6], (C, hidden), fc_std), dtype),
+        "fc2_b": _to(_normal(g[7], (C,), fc_std / 2), dtype),
+    }
+
+
 def make_workload(name: str, B: Optional[int] = None) -> Case:
     """The named workload; ``B`` overrides the batch (same per-image recipe)."""
     w = dict(WORKLOADS[name])
