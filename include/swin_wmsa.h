@@ -189,8 +189,9 @@ swin_status swin_wmsa_fwd_timed(const swin_wmsa_desc* desc, const void* x, const
  *   workspace, ws_bytes >= swin_block_workspace_size(desc): the attention's
  *   workspace plus four intermediates (three [B*H*W, C], one [B*H*W, hidden]).
  * Requires a valid attention descriptor, hidden a multiple of 32 (<= 16384),
- * C <= 512 (else SWIN_ERR_UNSUPPORTED); LayerNorms and GELU in float32; the
- * intermediates are stored in attn.dtype.
+ * C <= 512 (else SWIN_ERR_UNSUPPORTED), x, y, the workspace, the weights and the
+ * LayerNorm parameters 16-byte aligned (else SWIN_ERR_ALIGN); LayerNorms and
+ * GELU in float32; the intermediates are stored in attn.dtype.
  */
 typedef struct {
   swin_wmsa_desc attn;

@@ -15,11 +15,16 @@
 // with A = swin_wmsa_fwd and F(u) = GELU(u W1^T + b1) W2^T + b2 (exact GELU).
 //
 // Kernels: ln_kernel (one wave per token; the residual adds are fused into it
-// or into the second GEMM) and dense_kernel (the general matrix-core tile of
-// gemm_core.hpp with a bias / GELU / residual epilogue).
+// or into the second GEMM) and the dense layers: the persistent tiled GEMM of
+// gemm_tiled.hip (16-bit, N % 128 == 0, K in 256 .. 2048) or else dense_kernel
+// (the general matrix-core tile of gemm_core.hpp), both with a bias / GELU /
+// residual epilogue.
 #include <string.h>
 
+#include <type_traits>
+
 #include "gemm_core.hpp"
+#include "launch.hpp"
 #include "swin_wmsa.h"
 
 namespace swin {
@@ -32,48 +37,113 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-constexpr int kLnMaxPerLane = 8;  // C <= 512
+constexpr int kLnMaxC = 512;
+
+// Sum over the LPR consecutive lanes that share a row (LPR a power of two).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int d = LPR / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
 
 // v = a (+ b); u (if given) <- v; out <- LN(v) * gamma + beta (+ r).  LayerNorm
-// over the C channels of a token, biased variance, in float32.  One wave per
-// token row, four rows per workgroup.
-template <typename T>
+// over the C channels of a token, biased variance, in float32.  Each lane takes
+// one 16-byte chunk (8 channels) of a row, LPR lanes a row (C <= 8 LPR), so a
+// wave covers 64 / LPR rows with full-width loads and stores.
+template <typename T, int LPR>
 __global__ __launch_bounds__(256) void ln_kernel(const T* __restrict__ a, const T* __restrict__ b,
                                                  T* __restrict__ u, const T* __restrict__ gamma,
                                                  const T* __restrict__ beta,
                                                  const T* __restrict__ r, T* __restrict__ out,
                                                  int rows, int C, float eps) {
+  static_assert(sizeof(T) == 2, "16-bit rows");
+  constexpr int RPW = 64 / LPR;  // rows per wave
+  const int lane = threadIdx.x & 63;
+  const int row = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int c0 = 8 * (lane % LPR);
+  const bool live = row < rows && c0 < C;  // idle lanes still join the reductions
+  const int64_t o = (int64_t)row * C + c0;
+  float v[8];
+  float s = 0.f;
+  if (live) {
+    const vec8<T> av = gload8(a + o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)av[e];
+    if (b) {
+      const vec8<T> bv = gload8(b + o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] += (float)bv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += v[e];
+  }
+  const float mean = group_sum<LPR>(s) / (float)C;
+  float q = 0.f;
+  if (live) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q += (v[e] - mean) * (v[e] - mean);
+  }
+  const float rstd = 1.0f / sqrtf(group_sum<LPR>(q) / (float)C + eps);
+  if (!live) return;
+  if (u) {
+    vec8<T> uv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) uv[e] = (T)v[e];
+    gstore16(u + o, __builtin_bit_cast(uint4, uv));
+  }
+  const vec8<T> gv = gload8(gamma + c0), bev = gload8(beta + c0);
+  float z[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (v[e] - mean) * rstd * (float)gv[e] + (float)bev[e];
+  if (r) {
+    const vec8<T> rv = gload8(r + o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] += (float)rv[e];
+  }
+  vec8<T> zv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) zv[e] = (T)z[e];
+  gstore16(out + o, __builtin_bit_cast(uint4, zv));
+}
+
+// float32 rows: one wave per row, lane c, c + 64, ... (up to 8 per lane).
+template <>
+__global__ __launch_bounds__(256) void ln_kernel<float, 64>(
+    const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ u,
+    const float* __restrict__ gamma, const float* __restrict__ beta, const float* __restrict__ r,
+    float* __restrict__ out, int rows, int C, float eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int64_t base = (int64_t)row * C;
-  float v[kLnMaxPerLane];
+  float v[8];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < kLnMaxPerLane; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int c = lane + 64 * i;
     v[i] = 0.f;
     if (c < C) {
-      v[i] = (float)a[base + c] + (b ? (float)b[base + c] : 0.f);
+      v[i] = a[base + c] + (b ? b[base + c] : 0.f);
       s += v[i];
     }
   }
-  const float mean = wave_sum(s) / (float)C;
+  const float mean = group_sum<64>(s) / (float)C;
   float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < kLnMaxPerLane; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int c = lane + 64 * i;
     if (c < C) q += (v[i] - mean) * (v[i] - mean);
   }
-  const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)C + eps);
+  const float rstd = 1.0f / sqrtf(group_sum<64>(q) / (float)C + eps);
 #pragma unroll
-  for (int i = 0; i < kLnMaxPerLane; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int c = lane + 64 * i;
     if (c >= C) continue;
-    if (u) u[base + c] = (T)v[i];
-    float z = (v[i] - mean) * rstd * (float)gamma[c] + (float)beta[c];
-    if (r) z += (float)r[base + c];
-    out[base + c] = (T)z;
+    if (u) u[base + c] = v[i];
+    float z = (v[i] - mean) * rstd * gamma[c] + beta[c];
+    if (r) z += r[base + c];
+    out[base + c] = z;
   }
 }
 
@@ -114,14 +184,35 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(const T* __restrict__ A
 template <typename T>
 hipError_t launch_ln(const T* a, const T* b, T* u, const T* g, const T* be, const T* r, T* out,
                      int rows, int C, float eps, hipStream_t st) {
-  hipLaunchKernelGGL((ln_kernel<T>), dim3((rows + 3) / 4), dim3(256), 0, st, a, b, u, g, be, r,
-                     out, rows, C, eps);
+  if constexpr (sizeof(T) == 4) {
+    hipLaunchKernelGGL((ln_kernel<float, 64>), dim3((rows + 3) / 4), dim3(256), 0, st, a, b, u, g,
+                       be, r, out, rows, C, eps);
+  } else {
+    // Lanes per row: the next power of two of C / 8 (16-byte chunks per row).
+    const int chunks = C / 8;
+    auto go = [&](auto lpr) {
+      constexpr int L = decltype(lpr)::value;
+      const int per_wg = 4 * (64 / L);
+      hipLaunchKernelGGL((ln_kernel<T, L>), dim3((rows + per_wg - 1) / per_wg), dim3(256), 0, st,
+                         a, b, u, g, be, r, out, rows, C, eps);
+    };
+    if (chunks <= 4) go(std::integral_constant<int, 4>());
+    else if (chunks <= 8) go(std::integral_constant<int, 8>());
+    else if (chunks <= 16) go(std::integral_constant<int, 16>());
+    else if (chunks <= 32) go(std::integral_constant<int, 32>());
+    else go(std::integral_constant<int, 64>());
+  }
   return hipGetLastError();
 }
 
 template <typename T, bool GELU, bool RES>
 hipError_t launch_dense(const T* A, const T* Wt, const T* bias, const T* R, T* Y, int rows, int N,
                         int K, hipStream_t st) {
+  constexpr int io = __is_same(T, float) ? kF32 : __is_same(T, h16) ? kF16 : kBF16;
+  if (dense_tiled_supported(N, K, io)) {
+    DenseParams d{io, rows, N, K, A, Wt, bias, RES ? R : nullptr, Y};
+    return launch_dense_tiled(d, GELU, st);
+  }
   const int gx = (rows + kBM - 1) / kBM;
   if (N % 128 == 0)
     hipLaunchKernelGGL((dense_kernel<T, 128, GELU, RES>), dim3(gx, N / 128), dim3(kThreads), 0,
@@ -231,7 +322,7 @@ swin_status swin_block_fwd(const swin_block_desc* d, const void* x, const swin_b
   if (at.B == 0) return SWIN_OK;
   if (swin_wmsa_kernel_count(&at) == 0) return SWIN_ERR_SHAPE;  // invalid attention desc
   if (d->hidden < 32 || d->hidden % 32 || d->hidden > 16384) return SWIN_ERR_SHAPE;
-  if (at.C > 64 * kLnMaxPerLane) return SWIN_ERR_UNSUPPORTED;
+  if (at.C > kLnMaxC) return SWIN_ERR_UNSUPPORTED;
   if (!x || !y || !workspace || !p->w_qkv || !p->w_proj || !p->bias_table || !p->ln1_g ||
       !p->ln1_b || !p->ln2_g || !p->ln2_b || !p->fc1_w || !p->fc2_w)
     return SWIN_ERR_NULL;
@@ -247,7 +338,8 @@ swin_status swin_block_fwd(const swin_block_desc* d, const void* x, const swin_b
       overlaps(workspace, L.total, p->fc2_w, hid * C * e))
     return SWIN_ERR_ALIAS;
   if (!al16(x) || !al16(y) || !al16(workspace) || !al16(p->fc1_w) || !al16(p->fc2_w) ||
-      !al16(p->w_qkv) || !al16(p->w_proj))
+      !al16(p->w_qkv) || !al16(p->w_proj) || !al16(p->ln1_g) || !al16(p->ln1_b) ||
+      !al16(p->ln2_g) || !al16(p->ln2_b))
     return SWIN_ERR_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);

@@ -433,6 +433,81 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_tiled_kernel(FwdParams
                                            rowbytes, smem, ntiles, src, epi);
 }
 
+// ---------------------------------------------------------------------------
+// Dense layer of the block's MLP: Y = act(A W^T + bias) (+ R), A [rows, K] and
+// R / Y [rows, N] row-major, W [N, K] (nn.Linear layout).
+// ---------------------------------------------------------------------------
+template <typename T, int BM, int BN, int WGM, int WGN, int NK, bool GELU, bool RES>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void dense_tiled_kernel(DenseParams d) {
+  using G = Cfg<BM, BN, WGM, WGN>;
+  using Src = TileSrc<G::A_INS, true>;
+  __shared__ __attribute__((aligned(1024))) char smem[G::SMEM];
+  const int rows = d.rows, N = d.N;
+  const int ncol = N / BN;
+  const int ntiles = (rows + BM - 1) / BM * ncol;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave - (wave / WGN) * WGN;
+  const int g4 = lane >> 4, i16 = lane & 15;
+  const uint32_t cb = load_chunk_bytes();
+  const uint32_t rowbytes = (uint32_t)NK * kStageK * 2;
+
+  // Rows past the end of A read zeros (the buffer bound) and are not stored.
+  auto src = [&](int tile, Src& sr) {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    const int m0 = rb * BM, n0 = cbk * BN;
+    sr.a[0] = (uint32_t)(m0 + load_row<G::A_INS>(0)) * rowbytes + cb;
+    sr.b = (uint32_t)(n0 + load_row<G::B_INS>(0)) * rowbytes + cb;
+    sr.touch = (uint32_t)min(m0 + (int)threadIdx.x % BM, rows - 1) * rowbytes;
+  };
+  const T* bias = static_cast<const T*>(d.bias);
+  const T* R = static_cast<const T*>(d.res);
+  T* Y = static_cast<T*>(d.y);
+  auto epi = [&](int tile, f32x4 (&acc)[G::TM][G::TN]) {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    const int m0 = rb * BM, n0 = cbk * BN;
+    int rbase = m0 + wm * G::WM + i16;
+    int c00 = n0 + wn * G::WN;
+    // Opaque here: keeps the epilogue's loads and row arithmetic from being
+    // scheduled into the main loop, where they would hold registers.
+    asm volatile("" : "+v"(rbase), "+s"(c00));
+    c00 += 8 * g4;
+    float b[G::TN / 2][8];
+#pragma unroll
+    for (int jh = 0; jh < G::TN / 2; ++jh) load_bias8(bias, c00 + 32 * jh, b[jh]);
+    // lane: row 16i + i16; columns 32jh + 8 g4 + e.
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      const int row = rbase + 16 * i;
+      if (row >= rows) continue;
+#pragma unroll
+      for (int jh = 0; jh < G::TN / 2; ++jh) {
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[i][2 * jh][r] + b[jh][r];
+          v[4 + r] = acc[i][2 * jh + 1][r] + b[jh][4 + r];
+        }
+        const int64_t o = (int64_t)row * N + c00 + 32 * jh;
+        if constexpr (GELU) {
+          // GELU(v) = v * Phi(v) = v (1 + erf(v / sqrt 2)) / 2.
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = 0.5f * v[e] * (1.0f + erff(v[e] * 0.70710678118654752f));
+        }
+        if constexpr (RES) {
+          const vec8<T> rr = gload8(R + o);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += (float)rr[e];
+        }
+        store8(Y + o, v, 1.0f);
+      }
+    }
+  };
+  run_tiles<T, BM, BN, WGM, WGN, NK, true>(static_cast<const char*>(d.a), (uint32_t)rows * rowbytes,
+                                           static_cast<const char*>(d.w), (uint32_t)N * rowbytes,
+                                           rowbytes, smem, ntiles, src, epi);
+}
+
 int num_cus() {
   static int n = 0;
   if (n == 0) {
@@ -499,7 +574,49 @@ hipError_t proj_tiled_dispatch(const FwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename T, int NK, bool GELU, bool RES>
+void dense_tiled_launch(const DenseParams& d, hipStream_t st) {
+  const int big = (d.rows + 255) / 256 * (d.N / 256);
+  if (d.N % 256 == 0 && big >= 2 * num_cus()) {
+    hipLaunchKernelGGL((dense_tiled_kernel<T, 256, 256, 2, 2, NK, GELU, RES>),
+                       dim3(persistent_grid(big, 1)), dim3(256), 0, st, d);
+  } else {
+    const int small = (d.rows + 127) / 128 * (d.N / 128);
+    hipLaunchKernelGGL((dense_tiled_kernel<T, 128, 128, 2, 2, NK, GELU, RES>),
+                       dim3(persistent_grid(small, 2)), dim3(256), 0, st, d);
+  }
+}
+
+template <typename T, bool GELU, bool RES>
+hipError_t dense_tiled_k(const DenseParams& d, hipStream_t st) {
+  switch (d.K) {
+    case 256: dense_tiled_launch<T, 4, GELU, RES>(d, st); break;
+    case 512: dense_tiled_launch<T, 8, GELU, RES>(d, st); break;
+    case 1024: dense_tiled_launch<T, 16, GELU, RES>(d, st); break;
+    case 2048: dense_tiled_launch<T, 32, GELU, RES>(d, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dense_tiled_t(const DenseParams& d, bool gelu, hipStream_t st) {
+  if (gelu && !d.res) return dense_tiled_k<T, true, false>(d, st);
+  if (!gelu && d.res) return dense_tiled_k<T, false, true>(d, st);
+  if (!gelu && !d.res) return dense_tiled_k<T, false, false>(d, st);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+bool dense_tiled_supported(int N, int K, int io) {
+  return io != kF32 && N % 128 == 0 && (K == 256 || K == 512 || K == 1024 || K == 2048);
+}
+
+hipError_t launch_dense_tiled(const DenseParams& d, bool gelu, hipStream_t st) {
+  if (!dense_tiled_supported(d.N, d.K, d.io)) return hipErrorInvalidValue;
+  return d.io == kF16 ? dense_tiled_t<h16>(d, gelu, st) : dense_tiled_t<b16>(d, gelu, st);
+}
 
 bool tiled_gemm_supported(int C, int io) { return io != kF32 && (C == 256 || C == 512); }
 

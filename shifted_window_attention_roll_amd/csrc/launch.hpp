@@ -55,6 +55,20 @@ bool tiled_attn_supported(int M, int io);
 hipError_t launch_tiled_attn(const FwdParams& p, hipStream_t st);
 // QKV / projection GEMMs for 16-bit I/O and C in {256, 512} (32-bit offsets:
 // tokens * C * 2 must stay below 2^31).
+// Dense layer of the block's MLP on the tiled GEMM: y = act(a w^T + bias) (+ res);
+// a [rows, K], w [N, K], res / y [rows, N]; 16-bit, N % 128 == 0, K in {256,
+// 512, 1024, 2048}.
+struct DenseParams {
+  int io, rows, N, K;
+  const void* a;
+  const void* w;
+  const void* bias;  // [N] or null
+  const void* res;   // [rows, N] or null
+  void* y;
+};
+bool dense_tiled_supported(int N, int K, int io);
+hipError_t launch_dense_tiled(const DenseParams& d, bool gelu, hipStream_t st);
+
 bool tiled_gemm_supported(int C, int io);
 hipError_t launch_qkv_tiled(const FwdParams& p, hipStream_t st);
 hipError_t launch_proj_tiled(const FwdParams& p, hipStream_t st);
