@@ -18,7 +18,9 @@ Prints ONE JSON line on stdout (logs go to stderr) with:
                stream they run on,
   cpu_baseline the float64 CPU oracle timed on a bounded sample of the same
                workload on this host,
-  workloads    the same measurement for the other workload shapes.
+  workloads    the same measurement for the other workload shapes,
+  full_block   informational: the whole block forward (LayerNorms, attention,
+               MLP, residual adds) of each workload's last block.
 """
 from __future__ import annotations
 
@@ -312,6 +314,53 @@ def measure(name, steps, warmup, hip):
     return out
 
 
+def block_time(name, steps, warmup):
+    """Full block forward (LayerNorms, attention, MLP with hidden 4C, the
+    residual adds) on the workload's last block, timed like a step: average ms
+    per block forward and the rates that gives.  Informational: the headline
+    value is the attention step above."""
+    import torch
+    import shifted_window_attention_roll_amd as swin
+    import workloads
+    case = workloads.make_workload(name)
+    blk, dev = case.blocks[-1], "cuda"
+    if case.mode == "v1":
+        table = blk.table.to(dev)
+    else:
+        table = swin.cpb_table(blk.cpb_w1.to(dev), blk.cpb_b1.to(dev), blk.cpb_w2.to(dev),
+                               blk.cpb_b2.to(dev), case.M)
+    p = {"w_qkv": blk.w_qkv.to(dev), "b_qkv": blk.b_qkv.to(dev), "w_proj": blk.w_proj.to(dev),
+         "b_proj": blk.b_proj.to(dev), "table": table}
+    if blk.tau is not None:
+        p["tau"] = blk.tau.to(dev)
+    p.update({k: v.to(dev) for k, v in
+              workloads.make_block_params(case.C, case.dtype, 77, fc_std=0.02).items()})
+    x = case.x.to(dev)
+    out = torch.empty_like(x)
+    d = swin.make_block_desc(case.B, case.H, case.W, case.C, case.heads, case.M, blk.s,
+                             case.mode, x.dtype)
+    ws = torch.empty(swin.block_workspace_size(d), dtype=torch.uint8, device=dev)
+
+    def run():
+        swin.block_fwd(x, p, case.M, blk.s, case.heads, case.mode, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    T, C = case.tokens, case.C
+    flops = T * (flops_per_token(C, case.M * case.M) + 16 * C * C)
+    del x, out, ws, p
+    return {"block_ms": ms, "block_tokens_per_s": T / (ms * 1e-3),
+            "block_tflops": flops / (ms * 1e-3) / 1e12, "hidden": 4 * C}
+
+
 CALIB_BYTES = 256 << 20   # size of the plain device copy that calibrates the HBM counters
 CALIB_REPS = 4
 
@@ -420,6 +469,8 @@ def main():
     ap.add_argument("--workload", default=MAIN)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the informational full-block (LayerNorm + MLP) timings")
     ap.add_argument("--traffic-run", action="store_true",
                     help="run --steps steps and the counter calibration copies, print no JSON")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -432,7 +483,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every window is independent; sharding is described in DESIGN.md). "
+              "(every window is independent). "
               "Run with --gpus 1.", file=sys.stderr, flush=True)
         sys.exit(2)
 
@@ -452,6 +503,10 @@ def main():
     log(json.dumps({"workload": args.workload, **{k: main_res[k] for k in
                                                   ("tokens_per_s", "ms_per_step", "tflops",
                                                    "kernel_ms")}}))
+    blocks = {}
+    if not args.no_block:
+        blocks[args.workload] = block_time(args.workload, min(args.steps, 20), 3)
+        log(json.dumps({"workload": args.workload, **blocks[args.workload]}))
     others = {}
     if not args.no_others:
         for name in workloads.WORKLOADS:
@@ -462,6 +517,9 @@ def main():
             others[name] = {k: res[k] for k in ("tokens_per_s", "ms_per_step", "tflops",
                                                 "frac_of_mfma_peak", "kernel_ms", "roofline")}
             log(json.dumps({"workload": name, **others[name]}))
+            if not args.no_block:
+                blocks[name] = block_time(name, min(args.steps, 20), 3)
+                log(json.dumps({"workload": name, **blocks[name]}))
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
@@ -493,6 +551,7 @@ def main():
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
         "workloads": others,
+        "full_block": blocks,
         "source_digest": source_digest(),
     }
     del case
