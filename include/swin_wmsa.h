@@ -212,6 +212,47 @@ size_t swin_block_workspace_size(const swin_block_desc* d);
 swin_status swin_block_fwd(const swin_block_desc* d, const void* x, const swin_block_params* p,
                            void* y, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Backward pass of the attention sub-layer (training).
+ *   Pages: "Boosting Swin Transformer Speed", Training Optimization (the fused
+ *   MHA and the shift / partition kernels are training speed-ups, so the
+ *   sub-layer is differentiated through the projection, both attention
+ *   products, the softmax with bias and mask, the QKV projection and the index
+ *   maps); "Swin Transformer V2" summary, How It Works (cosine logits over
+ *   max(tau, 0.01) plus the position bias).
+ * Given dy = dL/dy for y = swin_wmsa_fwd(desc, x, ...), writes the gradients of
+ * x (desc->dtype, [B, H, W, C]) and, in float32, of w_qkv [3C, C], b_qkv [3C],
+ * w_proj [C, C], b_proj [C], the bias table [(2M-1)^2, heads] (V2: the table
+ * the forward consumes, i.e. the CPB output) and (V2) tau [heads]; the tau
+ * gradient is 0 for a head whose tau <= tau_min (the clamp is flat there).
+ * Every gradient output is overwritten (not accumulated into).  Inputs as in
+ * swin_wmsa_fwd (b_qkv may be NULL = zero; b_proj does not enter the gradients).
+ *   workspace, ws_bytes >= swin_wmsa_bwd_workspace_size(desc): x and dy in
+ *   window order, the recomputed q | k | v and attention output and their
+ *   gradients (float32); overwritten by every call.
+ * Requires a valid descriptor with M <= 16 (else SWIN_ERR_UNSUPPORTED);
+ * x, dy, dx, w_qkv, w_proj and the workspace 16-byte aligned (SWIN_ERR_ALIGN);
+ * no output overlapping an input, another output or the workspace
+ * (SWIN_ERR_ALIAS); dtau non-NULL in V2.  Computes in float32 throughout.
+ */
+typedef struct {
+  void* dx;        /* [B, H, W, C], desc->dtype                      */
+  float* dw_qkv;   /* [3C, C]                                        */
+  float* db_qkv;   /* [3C]                                           */
+  float* dw_proj;  /* [C, C]                                         */
+  float* db_proj;  /* [C]                                            */
+  float* dtable;   /* [(2M-1)^2, heads]                              */
+  float* dtau;     /* [heads]; V2 only (ignored and may be NULL in V1) */
+} swin_wmsa_grads;
+
+/* Workspace bytes of swin_wmsa_bwd (0 for an invalid descriptor or B == 0). */
+size_t swin_wmsa_bwd_workspace_size(const swin_wmsa_desc* desc);
+
+swin_status swin_wmsa_bwd(const swin_wmsa_desc* desc, const void* x, const void* w_qkv,
+                          const void* b_qkv, const void* w_proj, const float* bias_table,
+                          const float* tau, const void* dy, const swin_wmsa_grads* grads,
+                          void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

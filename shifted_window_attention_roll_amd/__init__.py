@@ -22,7 +22,8 @@ _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _EXPORTS = ("swin_status_str", "swin_abi_version", "swin_partition_shift", "swin_reverse_unshift",
             "swin_cpb_table", "swin_wmsa_workspace_size", "swin_wmsa_fwd",
             "swin_wmsa_kernel_count", "swin_wmsa_kernel_name", "swin_wmsa_fwd_timed",
-            "swin_block_workspace_size", "swin_block_fwd")
+            "swin_block_workspace_size", "swin_block_fwd", "swin_wmsa_bwd_workspace_size",
+            "swin_wmsa_bwd")
 
 
 class SwinDesc(ctypes.Structure):
@@ -40,6 +41,11 @@ class BlockParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w_qkv", "b_qkv", "w_proj", "b_proj", "bias_table", "tau", "ln1_g", "ln1_b",
                  "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dw_qkv", "db_qkv", "dw_proj", "db_proj", "dtable", "dtau")]
 
 
 _lib = None
@@ -82,6 +88,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swin_block_fwd.restype = st
     lib.swin_block_fwd.argtypes = [ctypes.POINTER(BlockDesc), vp, ctypes.POINTER(BlockParams), vp,
                                    vp, ctypes.c_size_t, vp]
+    lib.swin_wmsa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.swin_wmsa_bwd_workspace_size.argtypes = [ctypes.POINTER(SwinDesc)]
+    lib.swin_wmsa_bwd.restype = st
+    lib.swin_wmsa_bwd.argtypes = [ctypes.POINTER(SwinDesc), vp, vp, vp, vp, vp, vp, vp,
+                                  ctypes.POINTER(Grads), vp, ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -190,6 +201,39 @@ def wmsa_fwd(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv: Optional[torch.Tensor]
         arr = (ctypes.c_void_p * len(events))(*events)
         _check(lib.swin_wmsa_fwd_timed(*args, arr, len(events)))
     return out
+
+
+def bwd_workspace_size(desc: SwinDesc) -> int:
+    return int(load_library().swin_wmsa_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def wmsa_bwd(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv: Optional[torch.Tensor],
+             w_proj: torch.Tensor, bias_table: torch.Tensor, dy: torch.Tensor, M: int, s: int,
+             heads: int, mode: str = "v1", tau: Optional[torch.Tensor] = None,
+             scale: float = 0.0, tau_min: float = 0.0, grads: Optional[dict] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of the sub-layer for upstream gradient dy: a dict with dx (dtype
+    of x) and float32 dw_qkv, db_qkv, dw_proj, db_proj, dtable and (V2) dtau."""
+    B, H, W, C = x.shape
+    desc = make_desc(B, H, W, C, heads, M, s, mode, x.dtype, scale, tau_min)
+    dev = x.device
+    if grads is None:
+        f = dict(dtype=torch.float32, device=dev)
+        grads = {"dx": torch.empty_like(x), "dw_qkv": torch.empty(3 * C, C, **f),
+                 "db_qkv": torch.empty(3 * C, **f), "dw_proj": torch.empty(C, C, **f),
+                 "db_proj": torch.empty(C, **f),
+                 "dtable": torch.empty((2 * M - 1) ** 2, heads, **f)}
+        if mode == "v2":
+            grads["dtau"] = torch.empty(heads, **f)
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_size(desc), 1), dtype=torch.uint8, device=dev)
+    g = Grads(*[_ptr(grads.get(n)) for n in
+                ("dx", "dw_qkv", "db_qkv", "dw_proj", "db_proj", "dtable", "dtau")])
+    _check(load_library().swin_wmsa_bwd(
+        ctypes.byref(desc), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj), _ptr(bias_table),
+        _ptr(tau), _ptr(dy), ctypes.byref(g), _ptr(workspace), workspace.numel(),
+        _stream(stream)))
+    return grads
 
 
 def make_block_desc(B, H, W, C, heads, M, s, mode="v1", dtype=torch.bfloat16, hidden=None,

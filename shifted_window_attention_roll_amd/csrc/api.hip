@@ -313,3 +313,101 @@ swin_status swin_wmsa_fwd_timed(const swin_wmsa_desc* d, const void* x, const vo
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Backward pass.
+
+namespace {
+
+struct BwdLayout {
+  size_t xw, dyw, dxw, qkv, dout, o, dqkv, total;
+};
+
+BwdLayout bwd_layout(const swin_wmsa_desc* d) {
+  BwdLayout L{};
+  const size_t T = (size_t)d->B * d->H * d->W, C = d->C, e = elem_bytes(d->dtype);
+  L.xw = 0;
+  L.dyw = round_up(L.xw + T * C * e, 256);
+  L.dxw = round_up(L.dyw + T * C * e, 256);
+  L.qkv = round_up(L.dxw + T * C * e, 256);
+  L.dout = round_up(L.qkv + T * 3 * C * 4, 256);
+  L.o = round_up(L.dout + T * C * 4, 256);
+  L.dqkv = round_up(L.o + T * C * 4, 256);
+  L.total = round_up(L.dqkv + T * 3 * C * 4, 256);
+  return L;
+}
+
+swin_status validate_bwd_desc(const swin_wmsa_desc* d) {
+  swin_status st = validate_desc(d);
+  if (st != SWIN_OK) return st;
+  if (d->M > 16) return SWIN_ERR_UNSUPPORTED;
+  return SWIN_OK;
+}
+
+}  // namespace
+
+size_t swin_wmsa_bwd_workspace_size(const swin_wmsa_desc* d) {
+  if (validate_bwd_desc(d) != SWIN_OK || d->B == 0) return 0;
+  return bwd_layout(d).total;
+}
+
+swin_status swin_wmsa_bwd(const swin_wmsa_desc* d, const void* x, const void* w_qkv,
+                          const void* b_qkv, const void* w_proj, const float* bias_table,
+                          const float* tau, const void* dy, const swin_wmsa_grads* gr,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  swin_status st = validate_bwd_desc(d);
+  if (st != SWIN_OK) return st;
+  const bool v2 = d->mode == SWIN_V2;
+  if (!gr || !w_qkv || !w_proj || !bias_table || !gr->dw_qkv || !gr->db_qkv || !gr->dw_proj ||
+      !gr->db_proj || !gr->dtable)
+    return SWIN_ERR_NULL;
+  if (d->B > 0 && (!x || !dy || !gr->dx)) return SWIN_ERR_NULL;
+  if (v2 && (!tau || !gr->dtau)) return SWIN_ERR_NULL;
+  const BwdLayout L = bwd_layout(d);
+  if (d->B > 0 && !workspace) return SWIN_ERR_NULL;
+  if (d->B > 0 && ws_bytes < L.total) return SWIN_ERR_WORKSPACE;
+  const size_t e = elem_bytes(d->dtype), C = d->C;
+  const size_t act = (size_t)d->B * d->H * d->W * C * e;
+  const size_t R2 = (size_t)(2 * d->M - 1) * (2 * d->M - 1);
+  const size_t ws = d->B > 0 ? L.total : 0;
+  struct Span { const void* p; size_t n; };
+  const Span outs[] = {{gr->dx, act}, {gr->dw_qkv, 3 * C * C * 4}, {gr->db_qkv, 3 * C * 4},
+                       {gr->dw_proj, C * C * 4}, {gr->db_proj, C * 4},
+                       {gr->dtable, R2 * d->heads * 4}, {v2 ? gr->dtau : nullptr, d->heads * 4u}};
+  const Span ins[] = {{x, act}, {dy, act}, {w_qkv, 3 * C * C * e}, {b_qkv, 3 * C * e},
+                      {w_proj, C * C * e}, {bias_table, R2 * d->heads * 4},
+                      {v2 ? tau : nullptr, d->heads * 4u}, {workspace, ws}};
+  const int no = sizeof(outs) / sizeof(outs[0]), ni = sizeof(ins) / sizeof(ins[0]);
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j)
+      if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return SWIN_ERR_ALIAS;
+    for (int j = i + 1; j < no; ++j)
+      if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return SWIN_ERR_ALIAS;
+  }
+  if (overlap(x, act, workspace, ws) || overlap(dy, act, workspace, ws)) return SWIN_ERR_ALIAS;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(gr->dx) || !aligned16(w_qkv) ||
+      !aligned16(w_proj) || (ws > 0 && !aligned16(workspace)))
+    return SWIN_ERR_ALIGN;
+
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.g = make_geom(d->B, d->H, d->W, d->C, d->M, d->s, d->heads);
+  a.io = io_type(d);
+  a.v2 = v2;
+  a.scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)kHeadDim);
+  a.tau_min = d->tau_min > 0.0f ? d->tau_min : 0.01f;
+  a.eps = 1e-12f;
+  a.x = x; a.dy = dy; a.w_qkv = w_qkv; a.b_qkv = b_qkv; a.w_proj = w_proj;
+  a.table = bias_table; a.tau = tau;
+  a.dx = gr->dx; a.dw_qkv = gr->dw_qkv; a.db_qkv = gr->db_qkv; a.dw_proj = gr->dw_proj;
+  a.db_proj = gr->db_proj; a.dtable = gr->dtable; a.dtau = v2 ? gr->dtau : nullptr;
+  char* w = static_cast<char*>(workspace);
+  if (d->B > 0) {
+    a.xw = w + L.xw; a.dyw = w + L.dyw; a.dxw = w + L.dxw;
+    a.qkv = reinterpret_cast<float*>(w + L.qkv);
+    a.dout = reinterpret_cast<float*>(w + L.dout);
+    a.o = reinterpret_cast<float*>(w + L.o);
+    a.dqkv = reinterpret_cast<float*>(w + L.dqkv);
+  }
+  return from_hip(launch_backward(a, static_cast<hipStream_t>(stream)));
+}

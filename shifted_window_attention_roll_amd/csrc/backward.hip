@@ -1,0 +1,484 @@
+// Backward pass of the shifted-window attention sub-layer: from dL/dy to the
+// gradients of x, the QKV and projection weights and biases, the relative
+// position bias table and (V2) tau.
+//
+// Pages: "Boosting Swin Transformer Speed", Training Optimization (the fused
+// MHA and the shift / partition kernels serve training, so the sub-layer is
+// differentiated through all of them); "Swin Transformer V2" summary, How It
+// Works (cosine logits divided by max(tau, 0.01), plus the position bias).
+//
+// Pipeline (window order, row-major slots, float32 intermediates):
+//   xw  = partition+shift(x),  dyw = partition+shift(dy)        (index maps)
+//   qkv = xw Wqkv^T + bqkv,    do  = dyw Wp                      (bwd_gemm)
+//   per (window, head): recompute S, P and O; dq, dk, dv; table and tau
+//   gradients                                                     (attn_bwd)
+//   dWp = dyw^T o, dWqkv = dqkv^T xw (split over tokens, atomics) (bwd_gemm)
+//   dbp, dbqkv = column sums of dyw, dqkv                         (colsum)
+//   dxw = dqkv Wqkv, dx = reverse+unshift(dxw)                    (bwd_gemm,
+//                                                                   index map)
+// The inverse of a permutation is its adjoint, so the index maps of the
+// forward carry the gradients between the image and window orders.
+#include "launch.hpp"
+
+namespace swin {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int64_t i) { return (float)p[i]; }
+
+// C[m][n] (+)= sum_k A(m, k) B(k, n) (+ bias[n]) with element strides, float32
+// accumulation.  64 x 64 tile per workgroup, 4 x 4 per thread, K in steps of
+// 16 through LDS; blockIdx.z takes the K range [z*kc, (z+1)*kc).  ATOMIC adds
+// the tile into C (float) instead of storing it; then only z = 0 adds bias.
+constexpr int kGT = 64, kGK = 16;
+
+template <typename TA, typename TB, typename TC, bool ATOMIC>
+__global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm a) {
+  __shared__ float As[kGK][kGT + 4];
+  __shared__ float Bs[kGK][kGT + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int64_t m0 = (int64_t)blockIdx.y * kGT;
+  const int n0 = blockIdx.x * kGT;
+  const int64_t k0 = (int64_t)blockIdx.z * a.kc;
+  const int64_t k1 = k0 + a.kc < a.K ? k0 + a.kc : a.K;
+  const TA* A = static_cast<const TA*>(a.A);
+  const TB* B = static_cast<const TB*>(a.B);
+  const bool a_k_unit = a.sak == 1, b_n_unit = a.sbn == 1;
+  float acc[4][4] = {};
+  for (int64_t kb = k0; kb < k1; kb += kGK) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = tid + 256 * r;
+      // Consecutive threads walk the operand's unit-stride dimension.
+      const int kk = a_k_unit ? (e & 15) : (e >> 6);
+      const int mm = a_k_unit ? (e >> 4) : (e & 63);
+      const int64_t m = m0 + mm, k = kb + kk;
+      As[kk][mm] = (m < a.M && k < k1) ? ld(A, m * a.sam + k * a.sak) : 0.f;
+      const int kk2 = b_n_unit ? (e >> 6) : (e & 15);
+      const int nn = b_n_unit ? (e & 63) : (e >> 4);
+      const int n = n0 + nn;
+      const int64_t k2 = kb + kk2;
+      Bs[kk2][nn] = (n < a.N && k2 < k1) ? ld(B, k2 * a.sbk + (int64_t)n * a.sbn) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kGK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = As[kk][ty * 4 + i];
+        bv[i] = Bs[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  TC* C = static_cast<TC*>(a.C);
+  const bool add_bias = a.bias && (!ATOMIC || blockIdx.z == 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + ty * 4 + i;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= a.N) continue;
+      float v = acc[i][j];
+      if (add_bias) v += ld(static_cast<const TB*>(a.bias), n);
+      if constexpr (ATOMIC)
+        atomicAdd(reinterpret_cast<float*>(C) + m * a.ldc + n, v);
+      else
+        C[m * a.ldc + n] = from_f32<TC>(v);
+    }
+  }
+}
+
+// out[c] += sum over rows [z*rc, (z+1)*rc) of src[r*ld + c]; one column per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_kernel(const T* src, int64_t rows, int cols,
+                                                     int64_t ld, int64_t rc, float* out) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rc;
+  const int64_t r1 = r0 + rc < rows ? r0 + rc : rows;
+  float s = 0.f;
+  for (int64_t r = r0; r < r1; ++r) s += (float)src[r * ld + c];
+  atomicAdd(out + c, s);
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0.f;
+}
+
+// Per (window, head): recompute the attention and take its gradients.  One
+// workgroup per item; thread t owns query row t (phases 1-3) and key row t
+// (phase 4).  Rows of q, k, v and dO (32 floats) sit in LDS; the loops over
+// the other index read one row per step, the same for every lane (broadcast).
+//   phase 0: V2 normalises q and k (keeps the norms);
+//   phase 1: row max m_i and sum l_i of exp(S_ij - m_i) over allowed keys;
+//   phase 2: O_i = sum_j P_ij v_j (stored), D_i = dO_i . O_i;
+//   phase 3: dS_ij = P_ij (dO_i . v_j - D_i); dq_i; table and tau gradients;
+//   phase 4: dv_j = sum_i P_ij dO_i, dk_j = sum_i dS_ij q_i.
+// S_ij = c (q_i . k_j) + table[rel(i, j)], c = scale (V1) or 1 / max(tau,
+// tau_min) on unit q, k (V2).  Masked pairs (labels differ) are skipped: their
+// weight and gradient are zero.
+template <int NMAX, bool V2>
+__global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
+  constexpr int D = 32;
+  constexpr int TMAX = NMAX <= 64 ? 15 * 15 : 31 * 31;  // (2M-1)^2 for M <= 8, 16
+  __shared__ __attribute__((aligned(16))) float qs[NMAX][D];
+  __shared__ __attribute__((aligned(16))) float ks[NMAX][D];
+  __shared__ __attribute__((aligned(16))) float vs[NMAX][D];
+  __shared__ __attribute__((aligned(16))) float ds[NMAX][D];
+  __shared__ float rm[NMAX], rl[NMAX], rd[NMAX], qn[NMAX], kn[NMAX];
+  __shared__ int lab[NMAX];
+  __shared__ float tab[TMAX], dtab[TMAX];
+  __shared__ float red[NMAX / 64];
+
+  const Geom& g = p.g;
+  const int M = g.M, N = g.N, C = g.C, R = 2 * M - 1;
+  const int item = blockIdx.x;
+  const int w = item / g.heads, h = item - w * g.heads;
+  const int t = threadIdx.x;
+  const bool row = t < N;
+  const int64_t base = (int64_t)w * N;  // first window-order row of the window
+
+  // Region labels: only the last window row / column of the grid mixes two
+  // slices of the shifted frame, split at M - s.
+  const int wl = w % g.nW;
+  const int wy = wl / g.nWx, wx = wl - wy * g.nWx;
+  const bool my = g.s > 0 && wy == g.H / M - 1;
+  const bool mx = g.s > 0 && wx == g.nWx - 1;
+  const int ty = t / M, tx = t - (t / M) * M;
+  if (row) lab[t] = (my && ty >= M - g.s ? 2 : 0) + (mx && tx >= M - g.s ? 1 : 0);
+  for (int e = t; e < R * R; e += NMAX) {
+    tab[e] = p.table[(int64_t)e * g.heads + h];
+    dtab[e] = 0.f;
+  }
+  if (row) {
+    const float* src = p.qkv + (base + t) * 3 * C + h * D;
+    const float* dsrc = p.dout + (base + t) * C + h * D;
+#pragma unroll
+    for (int e = 0; e < D; e += 4) {
+      *reinterpret_cast<float4*>(&qs[t][e]) = *reinterpret_cast<const float4*>(src + e);
+      *reinterpret_cast<float4*>(&ks[t][e]) = *reinterpret_cast<const float4*>(src + C + e);
+      *reinterpret_cast<float4*>(&vs[t][e]) = *reinterpret_cast<const float4*>(src + 2 * C + e);
+      *reinterpret_cast<float4*>(&ds[t][e]) = *reinterpret_cast<const float4*>(dsrc + e);
+    }
+  }
+  float c = p.scale, t_eff = 1.f;
+  if constexpr (V2) {
+    t_eff = fmaxf(p.tau[h], p.tau_min);
+    c = 1.f / t_eff;
+    if (row) {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        sq = fmaf(qs[t][e], qs[t][e], sq);
+        sk = fmaf(ks[t][e], ks[t][e], sk);
+      }
+      const float nq = sqrtf(sq), nk = sqrtf(sk);
+      const float iq = 1.f / fmaxf(nq, p.eps), ik = 1.f / fmaxf(nk, p.eps);
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        qs[t][e] *= iq;
+        ks[t][e] *= ik;
+      }
+      qn[t] = nq;
+      kn[t] = nk;
+    }
+  }
+  __syncthreads();
+
+  auto rel = [&](int i, int j) {
+    const int yi = i / M, xi = i - yi * M, yj = j / M, xj = j - yj * M;
+    return (yi - yj + M - 1) * R + (xi - xj + M - 1);
+  };
+  auto dot = [&](const float (&a)[D], const float* b) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; e += 4) {
+      const float4 bv = *reinterpret_cast<const float4*>(b + e);
+      s = fmaf(a[e], bv.x, s);
+      s = fmaf(a[e + 1], bv.y, s);
+      s = fmaf(a[e + 2], bv.z, s);
+      s = fmaf(a[e + 3], bv.w, s);
+    }
+    return s;
+  };
+
+  float dtau_acc = 0.f;
+  if (row) {
+    const int i = t;
+    float qi[D], doi[D];
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      qi[e] = qs[i][e];
+      doi[e] = ds[i][e];
+    }
+    const int li = lab[i];
+    // Phase 1.
+    float m = -__builtin_inff(), l = 0.f;
+    for (int j = 0; j < N; ++j) {
+      if (lab[j] != li) continue;
+      const float sij = c * dot(qi, ks[j]) + tab[rel(i, j)];
+      const float mn = fmaxf(m, sij);
+      l = l * __expf(m - mn) + __expf(sij - mn);
+      m = mn;
+    }
+    const float il = 1.f / l;
+    // Phase 2.
+    float o[D] = {};
+    for (int j = 0; j < N; ++j) {
+      if (lab[j] != li) continue;
+      const float pij = __expf(c * dot(qi, ks[j]) + tab[rel(i, j)] - m) * il;
+#pragma unroll
+      for (int e = 0; e < D; ++e) o[e] = fmaf(pij, vs[j][e], o[e]);
+    }
+    float di = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) di = fmaf(doi[e], o[e], di);
+    float* og = p.o + (base + i) * C + h * D;
+#pragma unroll
+    for (int e = 0; e < D; e += 4)
+      *reinterpret_cast<float4*>(og + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+    rm[i] = m;
+    rl[i] = il;
+    rd[i] = di;
+    // Phase 3.
+    float dq[D] = {};
+    for (int j = 0; j < N; ++j) {
+      if (lab[j] != li) continue;
+      const float sim = dot(qi, ks[j]);
+      const int r = rel(i, j);
+      const float pij = __expf(c * sim + tab[r] - m) * il;
+      const float dsij = pij * (dot(doi, vs[j]) - di);
+#pragma unroll
+      for (int e = 0; e < D; ++e) dq[e] = fmaf(dsij, ks[j][e], dq[e]);
+      atomicAdd(&dtab[r], dsij);  // distinct i give distinct r for one j
+      if constexpr (V2) dtau_acc = fmaf(dsij, sim, dtau_acc);
+    }
+    float* dqg = p.dqkv + (base + i) * 3 * C + h * D;
+    if constexpr (V2) {
+      // dq_hat = c sum dS k_hat; through q_hat = q / max(|q|, eps).
+      float pr = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        dq[e] *= c;
+        pr = fmaf(qi[e], dq[e], pr);
+      }
+      const float nq = qn[i];
+      const bool big = nq > p.eps;
+      const float inv = 1.f / fmaxf(nq, p.eps);
+#pragma unroll
+      for (int e = 0; e < D; ++e) dq[e] = (big ? dq[e] - qi[e] * pr : dq[e]) * inv;
+    } else {
+#pragma unroll
+      for (int e = 0; e < D; ++e) dq[e] *= c;
+    }
+#pragma unroll
+    for (int e = 0; e < D; e += 4)
+      *reinterpret_cast<float4*>(dqg + e) = make_float4(dq[e], dq[e + 1], dq[e + 2], dq[e + 3]);
+  }
+  __syncthreads();  // row statistics complete, table gradient complete
+
+  if (row) {
+    // Phase 4, thread t owns key row j = t.
+    const int j = t;
+    float kj[D], vj[D];
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      kj[e] = ks[j][e];
+      vj[e] = vs[j][e];
+    }
+    const int lj = lab[j];
+    float dk[D] = {}, dv[D] = {};
+    for (int i = 0; i < N; ++i) {
+      if (lab[i] != lj) continue;
+      const float pij = __expf(c * dot(kj, qs[i]) + tab[rel(i, j)] - rm[i]) * rl[i];
+      const float dsij = pij * (dot(vj, ds[i]) - rd[i]);
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        dv[e] = fmaf(pij, ds[i][e], dv[e]);
+        dk[e] = fmaf(dsij, qs[i][e], dk[e]);
+      }
+    }
+    if constexpr (V2) {
+      float pr = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        dk[e] *= c;
+        pr = fmaf(kj[e], dk[e], pr);
+      }
+      const float nk = kn[j];
+      const bool big = nk > p.eps;
+      const float inv = 1.f / fmaxf(nk, p.eps);
+#pragma unroll
+      for (int e = 0; e < D; ++e) dk[e] = (big ? dk[e] - kj[e] * pr : dk[e]) * inv;
+    } else {
+#pragma unroll
+      for (int e = 0; e < D; ++e) dk[e] *= c;
+    }
+    float* dkg = p.dqkv + (base + j) * 3 * C + C + h * D;
+#pragma unroll
+    for (int e = 0; e < D; e += 4) {
+      *reinterpret_cast<float4*>(dkg + e) = make_float4(dk[e], dk[e + 1], dk[e + 2], dk[e + 3]);
+      *reinterpret_cast<float4*>(dkg + C + e) = make_float4(dv[e], dv[e + 1], dv[e + 2], dv[e + 3]);
+    }
+  }
+  for (int e = t; e < R * R; e += NMAX) atomicAdd(p.dtable + (int64_t)e * g.heads + h, dtab[e]);
+  if constexpr (V2) {
+    // d(t_eff) = -sum dS cos / t_eff^2, passed to tau where tau > tau_min.
+    float v = dtau_acc;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+    if ((t & 63) == 0) red[t >> 6] = v;
+    __syncthreads();
+    if (t == 0 && p.tau[h] > p.tau_min) {
+      float s = 0.f;
+      for (int k = 0; k < NMAX / 64; ++k) s += red[k];
+      atomicAdd(p.dtau + h, -s / (t_eff * t_eff));
+    }
+  }
+}
+
+template <typename TA, typename TB, typename TC, bool ATOMIC>
+hipError_t gemm_launch(const BwdGemm& a, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipSuccess;
+  BwdGemm b = a;
+  int splits = 1;
+  if (ATOMIC) {
+    // Split the reduction so that the grid fills the chip (about 2048 groups).
+    const int64_t tiles = ((a.M + kGT - 1) / kGT) * (int64_t)((a.N + kGT - 1) / kGT);
+    int64_t want = 2048 / (tiles > 0 ? tiles : 1);
+    if (want < 1) want = 1;
+    int64_t kc = (a.K + want - 1) / want;
+    kc = (kc + kGK - 1) / kGK * kGK;
+    b.kc = kc;
+    splits = (int)((a.K + kc - 1) / kc);
+  } else {
+    b.kc = a.K;
+  }
+  const dim3 grid((a.N + kGT - 1) / kGT, (unsigned)((a.M + kGT - 1) / kGT), splits);
+  hipLaunchKernelGGL((bwd_gemm_kernel<TA, TB, TC, ATOMIC>), grid, dim3(256), 0, st, b);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t colsum_launch(const T* src, int64_t rows, int cols, int64_t ld, float* out,
+                         hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const int cb = (cols + 255) / 256;
+  int64_t splits = 2048 / cb;
+  if (splits > rows) splits = rows;
+  if (splits < 1) splits = 1;
+  const int64_t rc = (rows + splits - 1) / splits;
+  splits = (rows + rc - 1) / rc;
+  hipLaunchKernelGGL((colsum_kernel<T>), dim3(cb, (unsigned)splits), dim3(256), 0, st, src, rows,
+                     cols, ld, rc, out);
+  return hipGetLastError();
+}
+
+hipError_t zero(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+#define TRY(x)                        \
+  do {                                \
+    hipError_t e_ = (x);              \
+    if (e_ != hipSuccess) return e_;  \
+  } while (0)
+
+template <typename T>
+hipError_t backward(const BwdArgs& a, hipStream_t st) {
+  const Geom& g = a.g;
+  const int C = g.C;
+  const int64_t T_ = (int64_t)g.B * g.H * g.W;
+  const int eb = (int)sizeof(T);
+  const int R2 = (2 * g.M - 1) * (2 * g.M - 1);
+  // Gradients that are accumulated start at zero.
+  TRY(zero(a.dw_qkv, 3LL * C * C, st));
+  TRY(zero(a.db_qkv, 3LL * C, st));
+  TRY(zero(a.dw_proj, (int64_t)C * C, st));
+  TRY(zero(a.db_proj, C, st));
+  TRY(zero(a.dtable, (int64_t)R2 * g.heads, st));
+  if (a.v2) TRY(zero(a.dtau, g.heads, st));
+  if (T_ == 0) return hipSuccess;
+  // Window order of x and dy.
+  TRY(launch_partition_shift(a.x, a.xw, g, eb, st));
+  TRY(launch_partition_shift(a.dy, a.dyw, g, eb, st));
+  // qkv = xw Wqkv^T + bqkv   [T, 3C]
+  BwdGemm q{};
+  q.M = T_; q.N = 3 * C; q.K = C;
+  q.A = a.xw; q.sam = C; q.sak = 1;
+  q.B = a.w_qkv; q.sbk = 1; q.sbn = C;
+  q.bias = a.b_qkv; q.C = a.qkv; q.ldc = 3 * C;
+  TRY((gemm_launch<T, T, float, false>(q, st)));
+  // do = dyw Wp   [T, C]   (y = o Wp^T + bp)
+  BwdGemm d{};
+  d.M = T_; d.N = C; d.K = C;
+  d.A = a.dyw; d.sam = C; d.sak = 1;
+  d.B = a.w_proj; d.sbk = C; d.sbn = 1;
+  d.C = a.dout; d.ldc = C;
+  TRY((gemm_launch<T, T, float, false>(d, st)));
+  // Attention backward per (window, head).
+  AttnBwd p{};
+  p.g = g; p.scale = a.scale; p.tau_min = a.tau_min; p.eps = a.eps;
+  p.qkv = a.qkv; p.dout = a.dout; p.table = a.table; p.tau = a.tau;
+  p.o = a.o; p.dqkv = a.dqkv; p.dtable = a.dtable; p.dtau = a.dtau;
+  const int items = g.B * g.nW * g.heads;
+  if (g.N <= 64) {
+    if (a.v2) hipLaunchKernelGGL((attn_bwd_kernel<64, true>), dim3(items), dim3(64), 0, st, p);
+    else hipLaunchKernelGGL((attn_bwd_kernel<64, false>), dim3(items), dim3(64), 0, st, p);
+  } else {
+    if (a.v2) hipLaunchKernelGGL((attn_bwd_kernel<256, true>), dim3(items), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((attn_bwd_kernel<256, false>), dim3(items), dim3(256), 0, st, p);
+  }
+  TRY(hipGetLastError());
+  // dWp = dyw^T o   [C, C];  dbp = colsum(dyw)
+  BwdGemm wp{};
+  wp.M = C; wp.N = C; wp.K = T_;
+  wp.A = a.dyw; wp.sam = 1; wp.sak = C;
+  wp.B = a.o; wp.sbk = C; wp.sbn = 1;
+  wp.C = a.dw_proj; wp.ldc = C;
+  TRY((gemm_launch<T, float, float, true>(wp, st)));
+  TRY(colsum_launch<T>(static_cast<const T*>(a.dyw), T_, C, C, a.db_proj, st));
+  // dWqkv = dqkv^T xw   [3C, C];  dbqkv = colsum(dqkv)
+  BwdGemm wq{};
+  wq.M = 3 * C; wq.N = C; wq.K = T_;
+  wq.A = a.dqkv; wq.sam = 1; wq.sak = 3 * C;
+  wq.B = a.xw; wq.sbk = C; wq.sbn = 1;
+  wq.C = a.dw_qkv; wq.ldc = C;
+  TRY((gemm_launch<float, T, float, true>(wq, st)));
+  TRY(colsum_launch<float>(a.dqkv, T_, 3 * C, 3 * C, a.db_qkv, st));
+  // dxw = dqkv Wqkv   [T, C], then back to image order.
+  BwdGemm dx{};
+  dx.M = T_; dx.N = C; dx.K = 3 * C;
+  dx.A = a.dqkv; dx.sam = 3 * C; dx.sak = 1;
+  dx.B = a.w_qkv; dx.sbk = C; dx.sbn = 1;
+  dx.C = a.dxw; dx.ldc = C;
+  TRY((gemm_launch<float, T, T, false>(dx, st)));
+  TRY(launch_reverse_unshift(a.dxw, a.dx, g, eb, st));
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
+  if (a.g.M > 16 || a.g.C != 32 * a.g.heads) return hipErrorInvalidValue;
+  if (a.io == kF32) return backward<float>(a, st);
+  if (a.io == kF16) return backward<h16>(a, st);
+  return backward<b16>(a, st);
+}
+
+}  // namespace swin

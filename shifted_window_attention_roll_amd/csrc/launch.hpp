@@ -88,6 +88,45 @@ hipError_t launch_fused_w8(const FwdParams& p, hipStream_t st);
 hipError_t launch_fused_window(const FwdParams& p, hipStream_t st);
 
 // Largest window side the attention kernel stages in LDS for an element size.
+// Backward pass (backward.hip).  Element-strided GEMM C = A B (+ bias):
+// A(m, k) = A[m*sam + k*sak], B(k, n) = B[k*sbk + n*sbn], C row pitch ldc.
+struct BwdGemm {
+  int64_t M, N, K, kc;
+  const void* A;
+  int64_t sam, sak;
+  const void* B;
+  int64_t sbk, sbn;
+  const void* bias;  // [N], B's element type, or null
+  void* C;
+  int64_t ldc;
+};
+struct AttnBwd {
+  Geom g;
+  float scale, tau_min, eps;
+  const float* qkv;    // [T, 3C] window order, linear bias included
+  const float* dout;   // [T, C] gradient of the attention output
+  const float* table;  // [(2M-1)^2, heads]
+  const float* tau;    // [heads] (V2)
+  float* o;            // [T, C] recomputed attention output
+  float* dqkv;         // [T, 3C]
+  float* dtable;       // accumulated
+  float* dtau;         // accumulated (V2)
+};
+struct BwdArgs {
+  Geom g;
+  int io;
+  bool v2;
+  float scale, tau_min, eps;
+  const void *x, *dy, *w_qkv, *b_qkv, *w_proj;
+  const float *table, *tau;
+  void* dx;
+  float *dw_qkv, *db_qkv, *dw_proj, *db_proj, *dtable, *dtau;
+  // workspace
+  void *xw, *dyw, *dxw;
+  float *qkv, *dout, *o, *dqkv;
+};
+hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
+
 inline int max_window(int io_bytes) { return io_bytes == 4 ? 16 : 24; }
 
 }  // namespace swin

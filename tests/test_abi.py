@@ -206,3 +206,45 @@ def test_block_rejects_before_launch(lib):
     assert _block(lib, d, y=FAKE + 64) == ALIAS                              # y overlaps x
     assert _block(lib, d, x=FAKE + 8) == ALIGN
     assert lib.swin_block_fwd(None, FAKE, None, FAKE, FAKE, 0, None) == NULL
+
+
+def _bwd(lib, d, x=FAKE, wq=FAKE * 2, wp=FAKE * 3, tab=FAKE * 4, tau=FAKE * 5, dy=FAKE * 6,
+         grads=None, ws=FAKE * 64, ws_bytes=None, **g):
+    if ws_bytes is None:
+        ws_bytes = lib.swin_wmsa_bwd_workspace_size(ctypes.byref(d))
+    fields = dict(dx=FAKE * 8, dw_qkv=FAKE * 9, db_qkv=FAKE * 10, dw_proj=FAKE * 11,
+                  db_proj=FAKE * 12, dtable=FAKE * 13, dtau=FAKE * 14)
+    fields.update(g)
+    gr = swin.Grads(*[fields[n] for n in ("dx", "dw_qkv", "db_qkv", "dw_proj", "db_proj",
+                                          "dtable", "dtau")])
+    return lib.swin_wmsa_bwd(ctypes.byref(d), x, wq, None, wp, tab, tau, dy,
+                             None if grads == "null" else ctypes.byref(gr), ws, ws_bytes, None)
+
+
+def test_bwd_workspace_size(lib):
+    d = _desc(B=1)
+    T, C = 56 * 56, 96
+    parts = [T * C * 2] * 3 + [T * 3 * C * 4, T * C * 4, T * C * 4, T * 3 * C * 4]
+    assert swin.bwd_workspace_size(d) == sum((p + 255) // 256 * 256 for p in parts)
+    assert swin.bwd_workspace_size(_desc(B=0)) == 0
+    assert swin.bwd_workspace_size(_desc(H=48, W=48, M=24, s=0, dtype=torch.bfloat16)) == 0
+    assert swin.bwd_workspace_size(_desc(heads=1)) == 0
+
+
+def test_bwd_rejects_before_launch(lib):
+    d = _desc(B=1)
+    assert _bwd(lib, _desc(B=1, H=48, W=48, M=24, s=0, dtype=torch.bfloat16)) == UNSUP
+    assert _bwd(lib, _desc(B=1, heads=5)) == SHAPE
+    assert _bwd(lib, d, wq=None) == NULL
+    assert _bwd(lib, d, dy=None) == NULL
+    assert _bwd(lib, d, grads="null") == NULL
+    assert _bwd(lib, d, dtable=None) == NULL
+    assert _bwd(lib, _desc(B=1, mode="v2"), dtau=None) == NULL
+    assert _bwd(lib, d, ws_bytes=16) == WS
+    assert _bwd(lib, d, dx=FAKE + 64) == ALIAS                # dx overlaps x
+    assert _bwd(lib, d, dw_proj=FAKE * 9 + 4) == ALIAS        # two outputs overlap
+    assert _bwd(lib, d, dtable=FAKE * 64 + 256) == ALIAS      # output inside the workspace
+    assert _bwd(lib, d, x=FAKE + 8) == ALIGN
+    assert _bwd(lib, d, ws=FAKE * 64 + 8) == ALIGN
+    assert lib.swin_wmsa_bwd(None, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE, 0,
+                             None) == NULL

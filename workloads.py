@@ -166,6 +166,12 @@ def make_block_params(C: int, dtype: str, seed: int, hidden: Optional[int] = Non
     }
 
 
+def make_upstream_grad(shape, dtype: str, seed: int, std: float = 1.0) -> torch.Tensor:
+    """Seeded N(0, std) upstream gradient dL/dy of ``shape``, rounded to ``dtype``."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    return _to(_normal(rng, tuple(shape), std), dtype)
+
+
 def make_workload(name: str, B: Optional[int] = None) -> Case:
     """The named workload; ``B`` overrides the batch (same per-image recipe)."""
     w = dict(WORKLOADS[name])
