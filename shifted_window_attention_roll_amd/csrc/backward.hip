@@ -27,18 +27,49 @@ namespace {
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, int64_t i) { return (float)p[i]; }
 
+// v[0..8) = p[off .. off+8) as float for the first `valid` elements (<= 8), 0
+// after; one 16-byte (16-bit) or two (float) loads when all 8 are valid.  The
+// full-run path needs off % 8 == 0 and a 16-byte aligned p.
+template <typename T>
+__device__ __forceinline__ void load_run8(const T* p, int64_t off, int valid, float (&v)[8]) {
+  if (valid >= 8) {
+    if constexpr (sizeof(T) == 4) {
+      const float4 a = *reinterpret_cast<const float4*>(p + off);
+      const float4 b = *reinterpret_cast<const float4*>(p + off + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      const vec8<T> a = *reinterpret_cast<const vec8<T>*>(p + off);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = i < valid ? (float)p[off + i] : 0.f;
+  }
+}
+
+__device__ __forceinline__ void store_row8(float* d, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(d) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 // C[m][n] (+)= sum_k A(m, k) B(k, n) (+ bias[n]) with element strides, float32
-// accumulation.  64 x 64 tile per workgroup, 4 x 4 per thread, K in steps of
-// 16 through LDS; blockIdx.z takes the K range [z*kc, (z+1)*kc).  ATOMIC adds
-// the tile into C (float) instead of storing it; then only z = 0 adds bias.
-constexpr int kGT = 64, kGK = 16;
+// on the matrix cores (16x16x4 float32 products, eight per 32-deep step).
+// 64 x 64 tile per workgroup of 4 waves, 32 x 32 per wave; K in steps of 32
+// through LDS, both operands stored [row][k] (k contiguous) so that a lane's
+// fragment is two 16-byte reads; blockIdx.z takes the K range [z*kc,
+// (z+1)*kc).  ATOMIC adds the tile into C (float) instead of storing it; then
+// only z = 0 adds bias.
+constexpr int kGT = 64, kGK = 32, kGP = kGK + 4;
 
 template <typename TA, typename TB, typename TC, bool ATOMIC>
 __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm a) {
-  __shared__ float As[kGK][kGT + 4];
-  __shared__ float Bs[kGK][kGT + 4];
-  const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
+  __shared__ __attribute__((aligned(16))) float As[kGT * kGP];  // [m][k]
+  __shared__ __attribute__((aligned(16))) float Bs[kGT * kGP];  // [n][k]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int i16 = lane & 15, g4 = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.y * kGT;
   const int n0 = blockIdx.x * kGT;
   const int64_t k0 = (int64_t)blockIdx.z * a.kc;
@@ -46,55 +77,80 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm a) {
   const TA* A = static_cast<const TA*>(a.A);
   const TB* B = static_cast<const TB*>(a.B);
   const bool a_k_unit = a.sak == 1, b_n_unit = a.sbn == 1;
-  float acc[4][4] = {};
-  for (int64_t kb = k0; kb < k1; kb += kGK) {
+  f32x4 acc[2][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = tid + 256 * r;
-      // Consecutive threads walk the operand's unit-stride dimension.
-      const int kk = a_k_unit ? (e & 15) : (e >> 6);
-      const int mm = a_k_unit ? (e >> 4) : (e & 63);
-      const int64_t m = m0 + mm, k = kb + kk;
-      As[kk][mm] = (m < a.M && k < k1) ? ld(A, m * a.sam + k * a.sak) : 0.f;
-      const int kk2 = b_n_unit ? (e >> 6) : (e & 15);
-      const int nn = b_n_unit ? (e & 63) : (e >> 4);
-      const int n = n0 + nn;
-      const int64_t k2 = kb + kk2;
-      Bs[kk2][nn] = (n < a.N && k2 < k1) ? ld(B, k2 * a.sbk + (int64_t)n * a.sbn) : 0.f;
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t kb = k0; kb < k1; kb += kGK) {
+    // Each thread stages one run of 8 elements of each operand along its
+    // unit-stride dimension (k, or the row dimension m / n).
+    {
+      float v[8];
+      if (a_k_unit) {
+        const int mm = tid >> 2, kk = (tid & 3) * 8;
+        const int64_t m = m0 + mm, k = kb + kk;
+        load_run8(A, m * a.sam + k, m < a.M ? (int)min<int64_t>(k1 - k, 8) : 0, v);
+        store_row8(&As[mm * kGP + kk], v);
+      } else {
+        const int kk = tid >> 3, mm = (tid & 7) * 8;
+        const int64_t m = m0 + mm, k = kb + kk;
+        load_run8(A, m + k * a.sak, k < k1 ? (int)min<int64_t>(a.M - m, 8) : 0, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) As[(mm + i) * kGP + kk] = v[i];
+      }
+      if (!b_n_unit) {
+        const int nn = tid >> 2, kk = (tid & 3) * 8;
+        const int n = n0 + nn;
+        const int64_t k = kb + kk;
+        load_run8(B, (int64_t)n * a.sbn + k, n < a.N ? (int)min<int64_t>(k1 - k, 8) : 0, v);
+        store_row8(&Bs[nn * kGP + kk], v);
+      } else {
+        const int kk = tid >> 3, nn = (tid & 7) * 8;
+        const int n = n0 + nn;
+        const int64_t k = kb + kk;
+        load_run8(B, n + k * a.sbk, k < k1 ? (int)min<int64_t>(a.N - n, 8) : 0, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Bs[(nn + i) * kGP + kk] = v[i];
+      }
     }
     __syncthreads();
+    vec8<float> af[2], bf[2];
 #pragma unroll
-    for (int kk = 0; kk < kGK; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        av[i] = As[kk][ty * 4 + i];
-        bv[i] = Bs[kk][tx * 4 + i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    for (int i = 0; i < 2; ++i) {
+      const float* pa = &As[(wm * 32 + i * 16 + i16) * kGP + 8 * g4];
+      const float* pb = &Bs[(wn * 32 + i * 16 + i16) * kGP + 8 * g4];
+      const float4 a0 = *reinterpret_cast<const float4*>(pa);
+      const float4 a1 = *reinterpret_cast<const float4*>(pa + 4);
+      const float4 b0 = *reinterpret_cast<const float4*>(pb);
+      const float4 b1 = *reinterpret_cast<const float4*>(pb + 4);
+      af[i] = vec8<float>{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      bf[i] = vec8<float>{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mma_16x16x32(af[i], bf[j], acc[i][j]);
     __syncthreads();
   }
+  // Lane l holds column l % 16 of rows 4 (l / 16) .. +3 of each 16 x 16 tile.
   TC* C = static_cast<TC*>(a.C);
   const bool add_bias = a.bias && (!ATOMIC || blockIdx.z == 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + ty * 4 + i;
-    if (m >= a.M) continue;
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 32 + j * 16 + i16;
+    if (n >= a.N) continue;
+    const float bn = add_bias ? ld(static_cast<const TB*>(a.bias), n) : 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
-      if (n >= a.N) continue;
-      float v = acc[i][j];
-      if (add_bias) v += ld(static_cast<const TB*>(a.bias), n);
-      if constexpr (ATOMIC)
-        atomicAdd(reinterpret_cast<float*>(C) + m * a.ldc + n, v);
-      else
-        C[m * a.ldc + n] = from_f32<TC>(v);
-    }
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * 32 + i * 16 + 4 * g4 + r;
+        if (m >= a.M) continue;
+        const float v = acc[i][j][r] + bn;
+        if constexpr (ATOMIC)
+          atomicAdd(reinterpret_cast<float*>(C) + m * a.ldc + n, v);
+        else
+          C[m * a.ldc + n] = from_f32<TC>(v);
+      }
   }
 }
 
@@ -351,6 +407,10 @@ __global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
 template <typename TA, typename TB, typename TC, bool ATOMIC>
 hipError_t gemm_launch(const BwdGemm& a, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipSuccess;
+  // Staging reads runs of 8 along a unit stride of each operand.
+  if ((a.sak != 1 && a.sam != 1) || (a.sbn != 1 && a.sbk != 1)) return hipErrorInvalidValue;
+  if ((a.sak == 1 ? a.sam : a.sak) % 8 || (a.sbn == 1 ? a.sbk : a.sbn) % 8)
+    return hipErrorInvalidValue;
   BwdGemm b = a;
   int splits = 1;
   if (ATOMIC) {

@@ -89,7 +89,8 @@ hipError_t launch_fused_window(const FwdParams& p, hipStream_t st);
 
 // Largest window side the attention kernel stages in LDS for an element size.
 // Backward pass (backward.hip).  Element-strided GEMM C = A B (+ bias):
-// A(m, k) = A[m*sam + k*sak], B(k, n) = B[k*sbk + n*sbn], C row pitch ldc.
+// A(m, k) = A[m*sam + k*sak], B(k, n) = B[k*sbk + n*sbn], C row pitch ldc;
+// one stride of each operand is 1 and the other a multiple of 8.
 struct BwdGemm {
   int64_t M, N, K, kc;
   const void* A;
