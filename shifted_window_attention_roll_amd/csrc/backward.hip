@@ -174,8 +174,10 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
 
 // Per (window, head): recompute the attention and take its gradients.  One
 // workgroup per item; thread t owns query row t (phases 1-3) and key row t
-// (phase 4).  Rows of q, k, v and dO (32 floats) sit in LDS; the loops over
-// the other index read one row per step, the same for every lane (broadcast).
+// (phase 4), and keeps that row's q, dO (then k, v) in registers.  Two LDS
+// row buffers of 32 floats per token: K and V for phases 1-3, then Q and dO
+// for phase 4 (the loops over the other index read one row per step, the same
+// for every lane: a broadcast).
 //   phase 0: V2 normalises q and k (keeps the norms);
 //   phase 1: row max m_i and sum l_i of exp(S_ij - m_i) over allowed keys;
 //   phase 2: O_i = sum_j P_ij v_j (stored), D_i = dO_i . O_i;
@@ -185,14 +187,12 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
 // tau_min) on unit q, k (V2).  Masked pairs (labels differ) are skipped: their
 // weight and gradient are zero.
 template <int NMAX, bool V2>
-__global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
+__global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void attn_bwd_kernel(AttnBwd p) {
   constexpr int D = 32;
   constexpr int TMAX = NMAX <= 64 ? 15 * 15 : 31 * 31;  // (2M-1)^2 for M <= 8, 16
-  __shared__ __attribute__((aligned(16))) float qs[NMAX][D];
-  __shared__ __attribute__((aligned(16))) float ks[NMAX][D];
-  __shared__ __attribute__((aligned(16))) float vs[NMAX][D];
-  __shared__ __attribute__((aligned(16))) float ds[NMAX][D];
-  __shared__ float rm[NMAX], rl[NMAX], rd[NMAX], qn[NMAX], kn[NMAX];
+  __shared__ __attribute__((aligned(16))) float b0[NMAX][D];  // K, then Q
+  __shared__ __attribute__((aligned(16))) float b1[NMAX][D];  // V, then dO
+  __shared__ float rm[NMAX], rl[NMAX], rd[NMAX];
   __shared__ int lab[NMAX];
   __shared__ float tab[TMAX], dtab[TMAX];
   __shared__ float red[NMAX / 64];
@@ -217,38 +217,50 @@ __global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
     tab[e] = p.table[(int64_t)e * g.heads + h];
     dtab[e] = 0.f;
   }
-  if (row) {
-    const float* src = p.qkv + (base + t) * 3 * C + h * D;
-    const float* dsrc = p.dout + (base + t) * C + h * D;
-#pragma unroll
-    for (int e = 0; e < D; e += 4) {
-      *reinterpret_cast<float4*>(&qs[t][e]) = *reinterpret_cast<const float4*>(src + e);
-      *reinterpret_cast<float4*>(&ks[t][e]) = *reinterpret_cast<const float4*>(src + C + e);
-      *reinterpret_cast<float4*>(&vs[t][e]) = *reinterpret_cast<const float4*>(src + 2 * C + e);
-      *reinterpret_cast<float4*>(&ds[t][e]) = *reinterpret_cast<const float4*>(dsrc + e);
-    }
-  }
-  float c = p.scale, t_eff = 1.f;
+  // Own rows: q_t and dO_t in registers for phases 1-3; k_t and v_t go to LDS
+  // (and are read again from memory for phase 4).
+  float qi[D], doi[D];
+  float c = p.scale, t_eff = 1.f, nq = 0.f;
   if constexpr (V2) {
     t_eff = fmaxf(p.tau[h], p.tau_min);
     c = 1.f / t_eff;
-    if (row) {
-      float sq = 0.f, sk = 0.f;
+  }
+  const float* src = p.qkv + (base + t) * 3 * C + h * D;
+  // Row r of a 32-float head slice: 8 float4 loads into a register array.
+  auto load_row = [&](const float* g_, float (&v)[D]) {
 #pragma unroll
-      for (int e = 0; e < D; ++e) {
-        sq = fmaf(qs[t][e], qs[t][e], sq);
-        sk = fmaf(ks[t][e], ks[t][e], sk);
-      }
-      const float nq = sqrtf(sq), nk = sqrtf(sk);
-      const float iq = 1.f / fmaxf(nq, p.eps), ik = 1.f / fmaxf(nk, p.eps);
-#pragma unroll
-      for (int e = 0; e < D; ++e) {
-        qs[t][e] *= iq;
-        ks[t][e] *= ik;
-      }
-      qn[t] = nq;
-      kn[t] = nk;
+    for (int e = 0; e < D; e += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(g_ + e);
+      v[e] = a.x; v[e + 1] = a.y; v[e + 2] = a.z; v[e + 3] = a.w;
     }
+  };
+  // V2: v / max(|v|, eps) in place; returns |v|.
+  auto unit = [&](float (&v)[D]) {
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) sq = fmaf(v[e], v[e], sq);
+    const float n = sqrtf(sq), inv = 1.f / fmaxf(n, p.eps);
+#pragma unroll
+    for (int e = 0; e < D; ++e) v[e] *= inv;
+    return n;
+  };
+  auto store_row = [&](float* l_, const float (&v)[D]) {
+#pragma unroll
+    for (int e = 0; e < D; e += 4)
+      *reinterpret_cast<float4*>(l_ + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+  };
+  if (row) {
+    {
+      float kv[D];
+      load_row(src + C, kv);
+      if constexpr (V2) unit(kv);
+      store_row(b0[t], kv);
+      load_row(src + 2 * C, kv);
+      store_row(b1[t], kv);
+    }
+    load_row(src, qi);
+    load_row(p.dout + (base + t) * C + h * D, doi);
+    if constexpr (V2) nq = unit(qi);
   }
   __syncthreads();
 
@@ -256,6 +268,7 @@ __global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
     const int yi = i / M, xi = i - yi * M, yj = j / M, xj = j - yj * M;
     return (yi - yj + M - 1) * R + (xi - xj + M - 1);
   };
+  // a . b for a row b in LDS (16-byte reads).
   auto dot = [&](const float (&a)[D], const float* b) {
     float s = 0.f;
 #pragma unroll
@@ -268,22 +281,27 @@ __global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
     }
     return s;
   };
+  // acc += f * b for a row b in LDS.
+  auto axpy = [&](float (&acc)[D], float f, const float* b) {
+#pragma unroll
+    for (int e = 0; e < D; e += 4) {
+      const float4 bv = *reinterpret_cast<const float4*>(b + e);
+      acc[e] = fmaf(f, bv.x, acc[e]);
+      acc[e + 1] = fmaf(f, bv.y, acc[e + 1]);
+      acc[e + 2] = fmaf(f, bv.z, acc[e + 2]);
+      acc[e + 3] = fmaf(f, bv.w, acc[e + 3]);
+    }
+  };
 
   float dtau_acc = 0.f;
   if (row) {
     const int i = t;
-    float qi[D], doi[D];
-#pragma unroll
-    for (int e = 0; e < D; ++e) {
-      qi[e] = qs[i][e];
-      doi[e] = ds[i][e];
-    }
     const int li = lab[i];
     // Phase 1.
     float m = -__builtin_inff(), l = 0.f;
     for (int j = 0; j < N; ++j) {
       if (lab[j] != li) continue;
-      const float sij = c * dot(qi, ks[j]) + tab[rel(i, j)];
+      const float sij = c * dot(qi, b0[j]) + tab[rel(i, j)];
       const float mn = fmaxf(m, sij);
       l = l * __expf(m - mn) + __expf(sij - mn);
       m = mn;
@@ -293,9 +311,8 @@ __global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
     float o[D] = {};
     for (int j = 0; j < N; ++j) {
       if (lab[j] != li) continue;
-      const float pij = __expf(c * dot(qi, ks[j]) + tab[rel(i, j)] - m) * il;
-#pragma unroll
-      for (int e = 0; e < D; ++e) o[e] = fmaf(pij, vs[j][e], o[e]);
+      const float pij = __expf(c * dot(qi, b0[j]) + tab[rel(i, j)] - m) * il;
+      axpy(o, pij, b1[j]);
     }
     float di = 0.f;
 #pragma unroll
@@ -311,12 +328,12 @@ __global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
     float dq[D] = {};
     for (int j = 0; j < N; ++j) {
       if (lab[j] != li) continue;
-      const float sim = dot(qi, ks[j]);
+      const float sim = dot(qi, b0[j]);
       const int r = rel(i, j);
       const float pij = __expf(c * sim + tab[r] - m) * il;
-      const float dsij = pij * (dot(doi, vs[j]) - di);
-#pragma unroll
-      for (int e = 0; e < D; ++e) dq[e] = fmaf(dsij, ks[j][e], dq[e]);
+      const float dsij = pij * (dot(doi, b1[j]) - di);
+      asm volatile("" ::: "memory");  // read the K row again: fewer live registers
+      axpy(dq, dsij, b0[j]);
       atomicAdd(&dtab[r], dsij);  // distinct i give distinct r for one j
       if constexpr (V2) dtau_acc = fmaf(dsij, sim, dtau_acc);
     }
@@ -329,7 +346,6 @@ __global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
         dq[e] *= c;
         pr = fmaf(qi[e], dq[e], pr);
       }
-      const float nq = qn[i];
       const bool big = nq > p.eps;
       const float inv = 1.f / fmaxf(nq, p.eps);
 #pragma unroll
@@ -342,41 +358,41 @@ __global__ __launch_bounds__(NMAX) void attn_bwd_kernel(AttnBwd p) {
     for (int e = 0; e < D; e += 4)
       *reinterpret_cast<float4*>(dqg + e) = make_float4(dq[e], dq[e + 1], dq[e + 2], dq[e + 3]);
   }
-  __syncthreads();  // row statistics complete, table gradient complete
+  __syncthreads();  // every read of K, V done; row statistics complete
+  if (row) {
+    store_row(b0[t], qi);
+    store_row(b1[t], doi);
+  }
+  __syncthreads();
 
   if (row) {
     // Phase 4, thread t owns key row j = t.
     const int j = t;
-    float kj[D], vj[D];
-#pragma unroll
-    for (int e = 0; e < D; ++e) {
-      kj[e] = ks[j][e];
-      vj[e] = vs[j][e];
-    }
+    float ki[D], vi[D], nk = 0.f;
+    load_row(src + C, ki);
+    load_row(src + 2 * C, vi);
+    if constexpr (V2) nk = unit(ki);
     const int lj = lab[j];
     float dk[D] = {}, dv[D] = {};
     for (int i = 0; i < N; ++i) {
       if (lab[i] != lj) continue;
-      const float pij = __expf(c * dot(kj, qs[i]) + tab[rel(i, j)] - rm[i]) * rl[i];
-      const float dsij = pij * (dot(vj, ds[i]) - rd[i]);
-#pragma unroll
-      for (int e = 0; e < D; ++e) {
-        dv[e] = fmaf(pij, ds[i][e], dv[e]);
-        dk[e] = fmaf(dsij, qs[i][e], dk[e]);
-      }
+      const float pij = __expf(c * dot(ki, b0[i]) + tab[rel(i, j)] - rm[i]) * rl[i];
+      const float dsij = pij * (dot(vi, b1[i]) - rd[i]);
+      asm volatile("" ::: "memory");  // read the rows again: fewer live registers
+      axpy(dv, pij, b1[i]);
+      axpy(dk, dsij, b0[i]);
     }
     if constexpr (V2) {
       float pr = 0.f;
 #pragma unroll
       for (int e = 0; e < D; ++e) {
         dk[e] *= c;
-        pr = fmaf(kj[e], dk[e], pr);
+        pr = fmaf(ki[e], dk[e], pr);
       }
-      const float nk = kn[j];
       const bool big = nk > p.eps;
       const float inv = 1.f / fmaxf(nk, p.eps);
 #pragma unroll
-      for (int e = 0; e < D; ++e) dk[e] = (big ? dk[e] - kj[e] * pr : dk[e]) * inv;
+      for (int e = 0; e < D; ++e) dk[e] = (big ? dk[e] - ki[e] * pr : dk[e]) * inv;
     } else {
 #pragma unroll
       for (int e = 0; e < D; ++e) dk[e] *= c;
