@@ -20,7 +20,9 @@ Prints ONE JSON line on stdout (logs go to stderr) with:
                workload on this host,
   workloads    the same measurement for the other workload shapes,
   full_block   informational: the whole block forward (LayerNorms, attention,
-               MLP, residual adds) of each workload's last block.
+               MLP, residual adds) of each workload's last block,
+  backward     informational: the attention sub-layer backward of each
+               workload's last block (windows up to 16; float32 compute).
 """
 from __future__ import annotations
 
@@ -361,6 +363,55 @@ def block_time(name, steps, warmup):
             "block_tflops": flops / (ms * 1e-3) / 1e12, "hidden": 4 * C}
 
 
+def backward_flops_per_token(C, N):
+    """Algorithmic flops per token of the sub-layer backward: the QKV recompute
+    6C^2, dO 2C^2, dWp 2C^2, dWqkv 6C^2, dx 6C^2; attention recompute (S, O) 4NC
+    and gradients (dP, dV, dQ, dK) 8NC."""
+    return 22 * C * C + 12 * N * C
+
+
+def backward_time(name, steps, warmup):
+    """Sub-layer backward (swin_wmsa_bwd) on the workload's last block, timed
+    like a step.  Informational: float32 throughout, so its roofline is the
+    float32 matrix-core peak."""
+    import torch
+    import shifted_window_attention_roll_amd as swin
+    import workloads
+    case = workloads.make_workload(name)
+    if case.M > 16:
+        return None
+    blk, dev = case.blocks[-1], "cuda"
+    if case.mode == "v1":
+        table = blk.table.to(dev)
+    else:
+        table = swin.cpb_table(blk.cpb_w1.to(dev), blk.cpb_b1.to(dev), blk.cpb_w2.to(dev),
+                               blk.cpb_b2.to(dev), case.M)
+    x = case.x.to(dev)
+    dy = workloads.make_upstream_grad(case.x.shape, case.dtype, 3).to(dev)
+    args = (x, blk.w_qkv.to(dev), blk.b_qkv.to(dev), blk.w_proj.to(dev), table, dy, case.M,
+            blk.s, case.heads, case.mode)
+    tau = None if blk.tau is None else blk.tau.to(dev)
+    d = swin.make_desc(case.B, case.H, case.W, case.C, case.heads, case.M, blk.s, case.mode,
+                       x.dtype)
+    ws = torch.empty(swin.bwd_workspace_size(d), dtype=torch.uint8, device=dev)
+    grads = swin.wmsa_bwd(*args, tau=tau, workspace=ws)
+    for _ in range(warmup):
+        swin.wmsa_bwd(*args, tau=tau, grads=grads, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        swin.wmsa_bwd(*args, tau=tau, grads=grads, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    T = case.tokens
+    tf = T * backward_flops_per_token(case.C, case.M * case.M) / (ms * 1e-3) / 1e12
+    del x, dy, ws, grads
+    return {"bwd_ms": ms, "bwd_tokens_per_s": T / (ms * 1e-3), "bwd_tflops": tf,
+            "bwd_frac_of_fp32_mfma_peak": tf / PEAK_TFLOPS["fp32"], "compute": "fp32"}
+
+
 CALIB_BYTES = 256 << 20   # size of the plain device copy that calibrates the HBM counters
 CALIB_REPS = 4
 
@@ -470,7 +521,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
     ap.add_argument("--no-block", action="store_true",
-                    help="skip the informational full-block (LayerNorm + MLP) timings")
+                    help="skip the informational full-block and backward timings")
     ap.add_argument("--traffic-run", action="store_true",
                     help="run --steps steps and the counter calibration copies, print no JSON")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -504,9 +555,12 @@ def main():
                                                   ("tokens_per_s", "ms_per_step", "tflops",
                                                    "kernel_ms")}}))
     blocks = {}
+    backs = {}
     if not args.no_block:
         blocks[args.workload] = block_time(args.workload, min(args.steps, 20), 3)
         log(json.dumps({"workload": args.workload, **blocks[args.workload]}))
+        backs[args.workload] = backward_time(args.workload, min(args.steps, 10), 2)
+        log(json.dumps({"workload": args.workload, "backward": backs[args.workload]}))
     others = {}
     if not args.no_others:
         for name in workloads.WORKLOADS:
@@ -520,6 +574,8 @@ def main():
             if not args.no_block:
                 blocks[name] = block_time(name, min(args.steps, 20), 3)
                 log(json.dumps({"workload": name, **blocks[name]}))
+                backs[name] = backward_time(name, min(args.steps, 10), 2)
+                log(json.dumps({"workload": name, "backward": backs[name]}))
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
@@ -552,6 +608,7 @@ def main():
         "cpu_baseline": cpu,
         "workloads": others,
         "full_block": blocks,
+        "backward": backs,
         "source_digest": source_digest(),
     }
     del case
