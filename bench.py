@@ -522,6 +522,8 @@ def main():
     ap.add_argument("--no-others", action="store_true", help="skip the other workload shapes")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the informational full-block and backward timings")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the sub-layer backward of --workload, print its JSON")
     ap.add_argument("--traffic-run", action="store_true",
                     help="run --steps steps and the counter calibration copies, print no JSON")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -546,6 +548,11 @@ def main():
     swin.load_library()
     if args.traffic_run:
         traffic_run(args.workload, args.steps)
+        return
+    if args.backward_only:
+        print(json.dumps({"workload": args.workload,
+                          "backward": backward_time(args.workload, args.steps, args.warmup)}),
+              flush=True)
         return
     hip = HipEvents()
 

@@ -186,6 +186,8 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
 // S_ij = c (q_i . k_j) + table[rel(i, j)], c = scale (V1) or 1 / max(tau,
 // tau_min) on unit q, k (V2).  Masked pairs (labels differ) are skipped: their
 // weight and gradient are zero.
+constexpr float kMasked = -1e30f;
+
 template <int NMAX, bool V2>
 __global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void attn_bwd_kernel(AttnBwd p) {
   constexpr int D = 32;
@@ -194,6 +196,8 @@ __global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void 
   __shared__ __attribute__((aligned(16))) float b1[NMAX][D];  // V, then dO
   __shared__ float rm[NMAX], rl[NMAX], rd[NMAX];
   __shared__ int lab[NMAX];
+  // rel(i, j) = ra[i] - rb[j]: ra = (y + M-1) R + x + M-1, rb = y R + x.
+  __shared__ int ra[NMAX], rb[NMAX];
   __shared__ float tab[TMAX], dtab[TMAX];
   __shared__ float red[NMAX / 64];
 
@@ -212,7 +216,11 @@ __global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void 
   const bool my = g.s > 0 && wy == g.H / M - 1;
   const bool mx = g.s > 0 && wx == g.nWx - 1;
   const int ty = t / M, tx = t - (t / M) * M;
-  if (row) lab[t] = (my && ty >= M - g.s ? 2 : 0) + (mx && tx >= M - g.s ? 1 : 0);
+  if (row) {
+    lab[t] = (my && ty >= M - g.s ? 2 : 0) + (mx && tx >= M - g.s ? 1 : 0);
+    ra[t] = (ty + M - 1) * R + tx + M - 1;
+    rb[t] = ty * R + tx;
+  }
   for (int e = t; e < R * R; e += NMAX) {
     tab[e] = p.table[(int64_t)e * g.heads + h];
     dtab[e] = 0.f;
@@ -264,10 +272,6 @@ __global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void 
   }
   __syncthreads();
 
-  auto rel = [&](int i, int j) {
-    const int yi = i / M, xi = i - yi * M, yj = j / M, xj = j - yj * M;
-    return (yi - yj + M - 1) * R + (xi - xj + M - 1);
-  };
   // a . b for a row b in LDS (16-byte reads).
   auto dot = [&](const float (&a)[D], const float* b) {
     float s = 0.f;
@@ -297,11 +301,15 @@ __global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void 
   if (row) {
     const int i = t;
     const int li = lab[i];
+    const int ai = ra[i];
     // Phase 1.
-    float m = -__builtin_inff(), l = 0.f;
+    // Masked pairs get the logit kMasked: exp underflows to exactly 0, so
+    // they add nothing, and the loops need no branch (the pair (i, i) is
+    // always allowed, so the row max is a real logit).
+    float m = kMasked, l = 0.f;
+#pragma unroll 2
     for (int j = 0; j < N; ++j) {
-      if (lab[j] != li) continue;
-      const float sij = c * dot(qi, b0[j]) + tab[rel(i, j)];
+      const float sij = lab[j] != li ? kMasked : c * dot(qi, b0[j]) + tab[ai - rb[j]];
       const float mn = fmaxf(m, sij);
       l = l * __expf(m - mn) + __expf(sij - mn);
       m = mn;
@@ -309,9 +317,10 @@ __global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void 
     const float il = 1.f / l;
     // Phase 2.
     float o[D] = {};
+#pragma unroll 2
     for (int j = 0; j < N; ++j) {
-      if (lab[j] != li) continue;
-      const float pij = __expf(c * dot(qi, b0[j]) + tab[rel(i, j)] - m) * il;
+      const float sij = lab[j] != li ? kMasked : c * dot(qi, b0[j]) + tab[ai - rb[j]];
+      const float pij = __expf(sij - m) * il;
       axpy(o, pij, b1[j]);
     }
     float di = 0.f;
@@ -326,11 +335,11 @@ __global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void 
     rd[i] = di;
     // Phase 3.
     float dq[D] = {};
+#pragma unroll 2
     for (int j = 0; j < N; ++j) {
-      if (lab[j] != li) continue;
       const float sim = dot(qi, b0[j]);
-      const int r = rel(i, j);
-      const float pij = __expf(c * sim + tab[r] - m) * il;
+      const int r = ai - rb[j];
+      const float pij = lab[j] != li ? 0.f : __expf(c * sim + tab[r] - m) * il;
       const float dsij = pij * (dot(doi, b1[j]) - di);
       asm volatile("" ::: "memory");  // read the K row again: fewer live registers
       axpy(dq, dsij, b0[j]);
@@ -373,10 +382,12 @@ __global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void 
     load_row(src + 2 * C, vi);
     if constexpr (V2) nk = unit(ki);
     const int lj = lab[j];
+    const int bj = rb[j];
     float dk[D] = {}, dv[D] = {};
+#pragma unroll 2
     for (int i = 0; i < N; ++i) {
-      if (lab[i] != lj) continue;
-      const float pij = __expf(c * dot(ki, b0[i]) + tab[rel(i, j)] - rm[i]) * rl[i];
+      const float sij = c * dot(ki, b0[i]) + tab[ra[i] - bj];
+      const float pij = lab[i] != lj ? 0.f : __expf(sij - rm[i]) * rl[i];
       const float dsij = pij * (dot(vi, b1[i]) - rd[i]);
       asm volatile("" ::: "memory");  // read the rows again: fewer live registers
       axpy(dv, pij, b1[i]);
