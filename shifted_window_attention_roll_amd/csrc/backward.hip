@@ -172,263 +172,378 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
     p[i] = 0.f;
 }
 
-// Per (window, head): recompute the attention and take its gradients.  One
-// workgroup per item; thread t owns query row t (phases 1-3) and key row t
-// (phase 4), and keeps that row's q, dO (then k, v) in registers.  Two LDS
-// row buffers of 32 floats per token: K and V for phases 1-3, then Q and dO
-// for phase 4 (the loops over the other index read one row per step, the same
-// for every lane: a broadcast).
-//   phase 0: V2 normalises q and k (keeps the norms);
-//   phase 1: row max m_i and sum l_i of exp(S_ij - m_i) over allowed keys;
-//   phase 2: O_i = sum_j P_ij v_j (stored), D_i = dO_i . O_i;
-//   phase 3: dS_ij = P_ij (dO_i . v_j - D_i); dq_i; table and tau gradients;
-//   phase 4: dv_j = sum_i P_ij dO_i, dk_j = sum_i dS_ij q_i.
+// Per (window, head): recompute the attention and take its gradients, every
+// product on the float32 matrix cores.  Phases:
+//   1: row max m_i and sum l_i of exp(S_ij - m_i) over allowed keys;
+//   2: P, dP, D_i = sum_j P_ij dP_ij, O = P V (stored);
+//   3: dS = P (dP - D); table (and V2 tau) gradients; dQ = dS K;
+//   4: dV = P^T dO, dK = dS^T Q.
 // S_ij = c (q_i . k_j) + table[rel(i, j)], c = scale (V1) or 1 / max(tau,
-// tau_min) on unit q, k (V2).  Masked pairs (labels differ) are skipped: their
-// weight and gradient are zero.
+// tau_min) on unit q, k (V2); masked pairs get the logit kMasked, whose
+// exponential underflows to exactly 0 (the pair (i, i) is always allowed).
+// One workgroup of NP/16 waves per (window, head); N is padded to NP (a multiple
+// of 32) with zero rows whose label matches only other padding rows, so they
+// stay finite and add nothing.  Wave w owns query tile w (16 rows) for
+// phases 1-3 and key tile w for phase 4.  Products are 16 x 16 tiles
+// (mma_16x16x32: lane l supplies row / column l % 16 and the K-slice
+// 8 (l/16) .. +7; the result holds column l % 16 of rows 4 (l/16) .. +3):
+//   S = Q K^T, dP = dO V^T (K-slice: head dims, fragments straight from rows);
+//   O = P V, dQ = dS K (K-slice: keys; P and dS go through a per-wave LDS
+//   tile to become row fragments, V and K are read as columns);
+//   S^T = K Q^T, dP^T = V dO^T, dV = P^T dO, dK = dS^T Q (phase 4).
+// LDS rows: K and V for phases 1-3, then Q and dO for phase 4.
 constexpr float kMasked = -1e30f;
 
-template <int NMAX, bool V2>
-__global__ __launch_bounds__(NMAX) __attribute__((amdgpu_waves_per_eu(3))) void attn_bwd_kernel(AttnBwd p) {
-  constexpr int D = 32;
-  constexpr int TMAX = NMAX <= 64 ? 15 * 15 : 31 * 31;  // (2M-1)^2 for M <= 8, 16
-  __shared__ __attribute__((aligned(16))) float b0[NMAX][D];  // K, then Q
-  __shared__ __attribute__((aligned(16))) float b1[NMAX][D];  // V, then dO
-  __shared__ float rm[NMAX], rl[NMAX], rd[NMAX];
-  __shared__ int lab[NMAX];
-  // rel(i, j) = ra[i] - rb[j]: ra = (y + M-1) R + x + M-1, rb = y R + x.
-  __shared__ int ra[NMAX], rb[NMAX];
+template <int NP, bool V2>
+__global__ __launch_bounds__(NP * 4) void attn_bwd_mfma_kernel(AttnBwd p) {
+  constexpr int D = 32, NWV = NP / 16, LD = D + 4;
+  constexpr int TMAX = NP <= 64 ? 15 * 15 : 31 * 31;
+  __shared__ __attribute__((aligned(16))) float b0[NP * LD];   // K, then Q
+  __shared__ __attribute__((aligned(16))) float b1[NP * LD];   // V, then dO
+  __shared__ __attribute__((aligned(16))) float stg[NWV][16 * LD];
+  __shared__ float rm[NP], rl[NP], rd[NP], nq[NP], nk[NP];
+  __shared__ int lab[NP], ra[NP], rb[NP];
   __shared__ float tab[TMAX], dtab[TMAX];
-  __shared__ float red[NMAX / 64];
+  __shared__ float red[NWV];
 
   const Geom& g = p.g;
-  const int M = g.M, N = g.N, C = g.C, R = 2 * M - 1;
+  const int M = g.M, N = g.N, C = g.C, R = 2 * M - 1, R2 = R * R;
   const int item = blockIdx.x;
   const int w = item / g.heads, h = item - w * g.heads;
-  const int t = threadIdx.x;
-  const bool row = t < N;
-  const int64_t base = (int64_t)w * N;  // first window-order row of the window
-
-  // Region labels: only the last window row / column of the grid mixes two
-  // slices of the shifted frame, split at M - s.
-  const int wl = w % g.nW;
-  const int wy = wl / g.nWx, wx = wl - wy * g.nWx;
-  const bool my = g.s > 0 && wy == g.H / M - 1;
-  const bool mx = g.s > 0 && wx == g.nWx - 1;
-  const int ty = t / M, tx = t - (t / M) * M;
-  if (row) {
-    lab[t] = (my && ty >= M - g.s ? 2 : 0) + (mx && tx >= M - g.s ? 1 : 0);
-    ra[t] = (ty + M - 1) * R + tx + M - 1;
-    rb[t] = ty * R + tx;
-  }
-  for (int e = t; e < R * R; e += NMAX) {
-    tab[e] = p.table[(int64_t)e * g.heads + h];
-    dtab[e] = 0.f;
-  }
-  // Own rows: q_t and dO_t in registers for phases 1-3; k_t and v_t go to LDS
-  // (and are read again from memory for phase 4).
-  float qi[D], doi[D];
-  float c = p.scale, t_eff = 1.f, nq = 0.f;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const int64_t base = (int64_t)w * N;
+  const float* qkv = p.qkv + h * D;
+  const float* dout = p.dout + h * D;
+  float c = p.scale, t_eff = 1.f;
   if constexpr (V2) {
     t_eff = fmaxf(p.tau[h], p.tau_min);
     c = 1.f / t_eff;
   }
-  const float* src = p.qkv + (base + t) * 3 * C + h * D;
-  // Row r of a 32-float head slice: 8 float4 loads into a register array.
-  auto load_row = [&](const float* g_, float (&v)[D]) {
-#pragma unroll
-    for (int e = 0; e < D; e += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(g_ + e);
-      v[e] = a.x; v[e + 1] = a.y; v[e + 2] = a.z; v[e + 3] = a.w;
-    }
-  };
-  // V2: v / max(|v|, eps) in place; returns |v|.
-  auto unit = [&](float (&v)[D]) {
+
+  const int wl = w % g.nW;
+  const int wy = wl / g.nWx, wx = wl - wy * g.nWx;
+  const bool my = g.s > 0 && wy == g.H / M - 1;
+  const bool mx = g.s > 0 && wx == g.nWx - 1;
+  for (int e = t; e < R2; e += NP * 4) {
+    tab[e] = p.table[(int64_t)e * g.heads + h];
+    dtab[e] = 0.f;
+  }
+  // Row t of a 32-float head slice (zeros for padding), V2 norm.
+  auto norm32 = [&](const float* src, float& n) {
     float sq = 0.f;
 #pragma unroll
-    for (int e = 0; e < D; ++e) sq = fmaf(v[e], v[e], sq);
-    const float n = sqrtf(sq), inv = 1.f / fmaxf(n, p.eps);
-#pragma unroll
-    for (int e = 0; e < D; ++e) v[e] *= inv;
-    return n;
-  };
-  auto store_row = [&](float* l_, const float (&v)[D]) {
-#pragma unroll
-    for (int e = 0; e < D; e += 4)
-      *reinterpret_cast<float4*>(l_ + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
-  };
-  if (row) {
-    {
-      float kv[D];
-      load_row(src + C, kv);
-      if constexpr (V2) unit(kv);
-      store_row(b0[t], kv);
-      load_row(src + 2 * C, kv);
-      store_row(b1[t], kv);
+    for (int e = 0; e < D; e += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(src + e);
+      sq = fmaf(a.x, a.x, fmaf(a.y, a.y, fmaf(a.z, a.z, fmaf(a.w, a.w, sq))));
     }
-    load_row(src, qi);
-    load_row(p.dout + (base + t) * C + h * D, doi);
-    if constexpr (V2) nq = unit(qi);
+    n = sqrtf(sq);
+    return 1.f / fmaxf(n, p.eps);
+  };
+  auto copy_row = [&](float* dst, const float* src, float mul) {
+#pragma unroll
+    for (int e = 0; e < D; e += 4) {
+      float4 a = src ? *reinterpret_cast<const float4*>(src + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      a.x *= mul; a.y *= mul; a.z *= mul; a.w *= mul;
+      *reinterpret_cast<float4*>(dst + e) = a;
+    }
+  };
+  if (t < NP) {
+    const bool real = t < N;
+    const int ty = real ? t / M : M - 1, tx = real ? t - (t / M) * M : M - 1;
+    lab[t] = real ? (my && ty >= M - g.s ? 2 : 0) + (mx && tx >= M - g.s ? 1 : 0) : 99;
+    ra[t] = (ty + M - 1) * R + tx + M - 1;
+    rb[t] = ty * R + tx;
+    const float* row = qkv + (base + t) * 3 * C;
+    float ik = 1.f, iq = 1.f, n0 = 0.f, n1 = 0.f;
+    if (V2 && real) {
+      ik = norm32(row + C, n1);
+      iq = norm32(row, n0);
+    }
+    nq[t] = n0;
+    nk[t] = n1;
+    copy_row(&b0[t * LD], real ? row + C : nullptr, ik);
+    copy_row(&b1[t * LD], real ? row + 2 * C : nullptr, 1.f);
   }
   __syncthreads();
 
-  // a . b for a row b in LDS (16-byte reads).
-  auto dot = [&](const float (&a)[D], const float* b) {
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < D; e += 4) {
-      const float4 bv = *reinterpret_cast<const float4*>(b + e);
-      s = fmaf(a[e], bv.x, s);
-      s = fmaf(a[e + 1], bv.y, s);
-      s = fmaf(a[e + 2], bv.z, s);
-      s = fmaf(a[e + 3], bv.w, s);
-    }
-    return s;
+  auto frag_row = [&](const float* r8) {  // 8 consecutive floats of an LDS row
+    const float4 a = *reinterpret_cast<const float4*>(r8);
+    const float4 b = *reinterpret_cast<const float4*>(r8 + 4);
+    return vec8<float>{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   };
-  // acc += f * b for a row b in LDS.
-  auto axpy = [&](float (&acc)[D], float f, const float* b) {
+  auto frag_col = [&](const float* buf, int row0, int col) {  // rows row0 .. +7 of a column
+    vec8<float> v;
 #pragma unroll
-    for (int e = 0; e < D; e += 4) {
-      const float4 bv = *reinterpret_cast<const float4*>(b + e);
-      acc[e] = fmaf(f, bv.x, acc[e]);
-      acc[e + 1] = fmaf(f, bv.y, acc[e + 1]);
-      acc[e + 2] = fmaf(f, bv.z, acc[e + 2]);
-      acc[e + 3] = fmaf(f, bv.w, acc[e + 3]);
-    }
+    for (int e = 0; e < 8; ++e) v[e] = buf[(row0 + e) * LD + col];
+    return v;
   };
+  // A fragment (row i16, K-slice 8 g4 .. +7) of a 32-float global row, scaled.
+  auto frag_glob = [&](const float* src, bool real, float mul) {
+    vec8<float> v = {};
+    if (real) {
+      const float4 a = *reinterpret_cast<const float4*>(src + 8 * g4);
+      const float4 b = *reinterpret_cast<const float4*>(src + 8 * g4 + 4);
+      v = vec8<float>{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= mul;
+    }
+    return v;
+  };
+  auto tidx = [&](int r) { return min(max(r, 0), R2 - 1); };
+  float* sw = stg[wave];
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
+  // ---- phases 1-3: query tile q0 ----
+  const int q0 = 16 * wave;
   float dtau_acc = 0.f;
-  if (row) {
-    const int i = t;
-    const int li = lab[i];
-    const int ai = ra[i];
-    // Phase 1.
-    // Masked pairs get the logit kMasked: exp underflows to exactly 0, so
-    // they add nothing, and the loops need no branch (the pair (i, i) is
-    // always allowed, so the row max is a real logit).
-    float m = kMasked, l = 0.f;
-#pragma unroll 2
-    for (int j = 0; j < N; ++j) {
-      const float sij = lab[j] != li ? kMasked : c * dot(qi, b0[j]) + tab[ai - rb[j]];
-      const float mn = fmaxf(m, sij);
-      l = l * __expf(m - mn) + __expf(sij - mn);
-      m = mn;
-    }
-    const float il = 1.f / l;
-    // Phase 2.
-    float o[D] = {};
-#pragma unroll 2
-    for (int j = 0; j < N; ++j) {
-      const float sij = lab[j] != li ? kMasked : c * dot(qi, b0[j]) + tab[ai - rb[j]];
-      const float pij = __expf(sij - m) * il;
-      axpy(o, pij, b1[j]);
-    }
-    float di = 0.f;
+  {
+    const int qa = q0 + i16;  // A-fragment row
+    const bool qa_real = qa < N;
+    const float* qrow = qkv + (base + qa) * 3 * C;
+    float qmul = 1.f;
+    if (V2 && qa_real) qmul = 1.f / fmaxf(nq[qa], p.eps);
+    const vec8<float> Qa = frag_glob(qrow, qa_real, qmul);
+    const vec8<float> DOa = frag_glob(dout + (base + qa) * C, qa_real, 1.f);
+    int labr[4], rar[4];
 #pragma unroll
-    for (int e = 0; e < D; ++e) di = fmaf(doi[e], o[e], di);
-    float* og = p.o + (base + i) * C + h * D;
-#pragma unroll
-    for (int e = 0; e < D; e += 4)
-      *reinterpret_cast<float4*>(og + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-    rm[i] = m;
-    rl[i] = il;
-    rd[i] = di;
-    // Phase 3.
-    float dq[D] = {};
-#pragma unroll 2
-    for (int j = 0; j < N; ++j) {
-      const float sim = dot(qi, b0[j]);
-      const int r = ai - rb[j];
-      const float pij = lab[j] != li ? 0.f : __expf(c * sim + tab[r] - m) * il;
-      const float dsij = pij * (dot(doi, b1[j]) - di);
-      asm volatile("" ::: "memory");  // read the K row again: fewer live registers
-      axpy(dq, dsij, b0[j]);
-      atomicAdd(&dtab[r], dsij);  // distinct i give distinct r for one j
-      if constexpr (V2) dtau_acc = fmaf(dsij, sim, dtau_acc);
+    for (int r = 0; r < 4; ++r) {
+      labr[r] = lab[q0 + 4 * g4 + r];
+      rar[r] = ra[q0 + 4 * g4 + r];
     }
-    float* dqg = p.dqkv + (base + i) * 3 * C + h * D;
-    if constexpr (V2) {
-      // dq_hat = c sum dS k_hat; through q_hat = q / max(|q|, eps).
-      float pr = 0.f;
+    auto logit = [&](float sraw, int r, int key) {
+      return lab[key] == labr[r] ? c * sraw + tab[tidx(rar[r] - rb[key])] : kMasked;
+    };
+    // Phase 1: online max / sum per row over the lane's key columns, then
+    // across the 16 lanes of the row group.
+    float m[4], l[4];
 #pragma unroll
-      for (int e = 0; e < D; ++e) {
-        dq[e] *= c;
-        pr = fmaf(qi[e], dq[e], pr);
+    for (int r = 0; r < 4; ++r) { m[r] = kMasked; l[r] = 0.f; }
+#pragma unroll 2
+    for (int kt = 0; kt < NWV; ++kt) {
+      const int key = 16 * kt + i16;
+      const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[key * LD + 8 * g4]), zero4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sv = logit(S[r], r, key);
+        const float mn = fmaxf(m[r], sv);
+        l[r] = l[r] * __expf(m[r] - mn) + __expf(sv - mn);
+        m[r] = mn;
       }
-      const bool big = nq > p.eps;
-      const float inv = 1.f / fmaxf(nq, p.eps);
-#pragma unroll
-      for (int e = 0; e < D; ++e) dq[e] = (big ? dq[e] - qi[e] * pr : dq[e]) * inv;
-    } else {
-#pragma unroll
-      for (int e = 0; e < D; ++e) dq[e] *= c;
     }
 #pragma unroll
-    for (int e = 0; e < D; e += 4)
-      *reinterpret_cast<float4*>(dqg + e) = make_float4(dq[e], dq[e + 1], dq[e + 2], dq[e + 3]);
+    for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mo = __shfl_xor(m[r], d), lo = __shfl_xor(l[r], d);
+        const float mn = fmaxf(m[r], mo);
+        l[r] = l[r] * __expf(m[r] - mn) + lo * __expf(mo - mn);
+        m[r] = mn;
+      }
+    float il[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) il[r] = 1.f / l[r];
+    // Phase 2: P, dP, D = rowsum(P dP); O = P V.
+    float dacc[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 o0 = zero4, o1 = zero4;
+#pragma unroll 1
+    for (int kb = 0; kb < NP / 32; ++kb) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int key = 32 * kb + 16 * tt + i16;
+        const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[key * LD + 8 * g4]), zero4);
+        const f32x4 dP = mma_16x16x32(DOa, frag_row(&b1[key * LD + 8 * g4]), zero4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = __expf(logit(S[r], r, key) - m[r]) * il[r];
+          dacc[r] = fmaf(pv, dP[r], dacc[r]);
+          sw[(4 * g4 + r) * LD + 16 * tt + i16] = pv;
+        }
+      }
+      asm volatile("" ::: "memory");
+      const vec8<float> Pa = frag_row(&sw[i16 * LD + 8 * g4]);
+      o0 = mma_16x16x32(Pa, frag_col(b1, 32 * kb + 8 * g4, i16), o0);
+      o1 = mma_16x16x32(Pa, frag_col(b1, 32 * kb + 8 * g4, 16 + i16), o1);
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dacc[r] += __shfl_xor(dacc[r], d);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = q0 + 4 * g4 + r;
+      if (i16 == 0) {
+        rm[q] = m[r];
+        rl[q] = il[r];
+        rd[q] = dacc[r];
+      }
+      if (q < N) {
+        float* og = p.o + (base + q) * C + h * D;
+        og[i16] = o0[r];
+        og[16 + i16] = o1[r];
+      }
+    }
+    // Phase 3: dS = P (dP - D); table (and tau) gradients; dQ = dS K.
+    f32x4 dq0 = zero4, dq1 = zero4;
+#pragma unroll 1
+    for (int kb = 0; kb < NP / 32; ++kb) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int key = 32 * kb + 16 * tt + i16;
+        const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[key * LD + 8 * g4]), zero4);
+        const f32x4 dP = mma_16x16x32(DOa, frag_row(&b1[key * LD + 8 * g4]), zero4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = lab[key] == labr[r];
+          const int ti = tidx(rar[r] - rb[key]);
+          const float pv = ok ? __expf(c * S[r] + tab[ti] - m[r]) * il[r] : 0.f;
+          const float ds = pv * (dP[r] - dacc[r]);
+          if (ok) atomicAdd(&dtab[ti], ds);
+          if constexpr (V2) dtau_acc = fmaf(ds, S[r], dtau_acc);
+          sw[(4 * g4 + r) * LD + 16 * tt + i16] = ds;
+        }
+      }
+      asm volatile("" ::: "memory");
+      const vec8<float> Sa = frag_row(&sw[i16 * LD + 8 * g4]);
+      dq0 = mma_16x16x32(Sa, frag_col(b0, 32 * kb + 8 * g4, i16), dq0);
+      dq1 = mma_16x16x32(Sa, frag_col(b0, 32 * kb + 8 * g4, 16 + i16), dq1);
+      asm volatile("" ::: "memory");
+    }
+    // dq (lane: dims i16 and 16 + i16 of rows q0 + 4 g4 + r).
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = q0 + 4 * g4 + r;
+      float a0 = c * dq0[r], a1 = c * dq1[r];
+      if constexpr (V2) {
+        // Through q_hat = q / max(|q|, eps): (dq_hat - q_hat (q_hat . dq_hat)) / |q|.
+        const bool real = q < N;
+        const float* qr = qkv + (base + (real ? q : 0)) * 3 * C;
+        const float inv = 1.f / fmaxf(nq[q], p.eps);
+        const float h0 = real ? qr[i16] * inv : 0.f, h1 = real ? qr[16 + i16] * inv : 0.f;
+        float pr = h0 * a0 + h1 * a1;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) pr += __shfl_xor(pr, d);
+        const bool big = nq[q] > p.eps;
+        a0 = (big ? a0 - h0 * pr : a0) * inv;
+        a1 = (big ? a1 - h1 * pr : a1) * inv;
+      }
+      if (q < N) {
+        float* dg = p.dqkv + (base + q) * 3 * C + h * D;
+        dg[i16] = a0;
+        dg[16 + i16] = a1;
+      }
+    }
   }
-  __syncthreads();  // every read of K, V done; row statistics complete
-  if (row) {
-    store_row(b0[t], qi);
-    store_row(b1[t], doi);
+  __syncthreads();  // K, V no longer read; row statistics complete
+  if (t < NP) {
+    const bool real = t < N;
+    const float* row = qkv + (base + t) * 3 * C;
+    copy_row(&b0[t * LD], real ? row : nullptr, V2 && real ? 1.f / fmaxf(nq[t], p.eps) : 1.f);
+    copy_row(&b1[t * LD], real ? dout + (base + t) * C : nullptr, 1.f);
   }
   __syncthreads();
 
-  if (row) {
-    // Phase 4, thread t owns key row j = t.
-    const int j = t;
-    float ki[D], vi[D], nk = 0.f;
-    load_row(src + C, ki);
-    load_row(src + 2 * C, vi);
-    if constexpr (V2) nk = unit(ki);
-    const int lj = lab[j];
-    const int bj = rb[j];
-    float dk[D] = {}, dv[D] = {};
-#pragma unroll 2
-    for (int i = 0; i < N; ++i) {
-      const float sij = c * dot(ki, b0[i]) + tab[ra[i] - bj];
-      const float pij = lab[i] != lj ? 0.f : __expf(sij - rm[i]) * rl[i];
-      const float dsij = pij * (dot(vi, b1[i]) - rd[i]);
-      asm volatile("" ::: "memory");  // read the rows again: fewer live registers
-      axpy(dv, pij, b1[i]);
-      axpy(dk, dsij, b0[i]);
-    }
-    if constexpr (V2) {
-      float pr = 0.f;
+  // ---- phase 4: key tile k0 ----
+  {
+    const int k0 = 16 * wave;
+    const int ka = k0 + i16;
+    const bool ka_real = ka < N;
+    const float* krow = qkv + (base + ka) * 3 * C;
+    float kmul = 1.f;
+    if (V2 && ka_real) kmul = 1.f / fmaxf(nk[ka], p.eps);
+    const vec8<float> Ka = frag_glob(krow + C, ka_real, kmul);
+    const vec8<float> Va = frag_glob(krow + 2 * C, ka_real, 1.f);
+    int labr[4], rbr[4];
 #pragma unroll
-      for (int e = 0; e < D; ++e) {
-        dk[e] *= c;
-        pr = fmaf(ki[e], dk[e], pr);
+    for (int r = 0; r < 4; ++r) {
+      labr[r] = lab[k0 + 4 * g4 + r];
+      rbr[r] = rb[k0 + 4 * g4 + r];
+    }
+    f32x4 dk0 = zero4, dk1 = zero4, dv0 = zero4, dv1 = zero4;
+#pragma unroll 1
+    for (int qb = 0; qb < NP / 32; ++qb) {
+      float pst[2][4], dst[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int q = 32 * qb + 16 * tt + i16;  // this lane's query column
+        const f32x4 ST = mma_16x16x32(Ka, frag_row(&b0[q * LD + 8 * g4]), zero4);
+        const f32x4 dPT = mma_16x16x32(Va, frag_row(&b1[q * LD + 8 * g4]), zero4);
+        const float mq = rm[q], ilq = rl[q], dq_ = rd[q];
+        const int labq = lab[q], raq = ra[q];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = labq == labr[r];
+          const float pv = ok ? __expf(c * ST[r] + tab[tidx(raq - rbr[r])] - mq) * ilq : 0.f;
+          pst[tt][r] = pv;
+          dst[tt][r] = pv * (dPT[r] - dq_);
+        }
       }
-      const bool big = nk > p.eps;
-      const float inv = 1.f / fmaxf(nk, p.eps);
 #pragma unroll
-      for (int e = 0; e < D; ++e) dk[e] = (big ? dk[e] - ki[e] * pr : dk[e]) * inv;
-    } else {
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int e = 0; e < D; ++e) dk[e] *= c;
+        for (int r = 0; r < 4; ++r) sw[(4 * g4 + r) * LD + 16 * tt + i16] = pst[tt][r];
+      asm volatile("" ::: "memory");
+      const vec8<float> Pa = frag_row(&sw[i16 * LD + 8 * g4]);
+      dv0 = mma_16x16x32(Pa, frag_col(b1, 32 * qb + 8 * g4, i16), dv0);
+      dv1 = mma_16x16x32(Pa, frag_col(b1, 32 * qb + 8 * g4, 16 + i16), dv1);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sw[(4 * g4 + r) * LD + 16 * tt + i16] = dst[tt][r];
+      asm volatile("" ::: "memory");
+      const vec8<float> Sa = frag_row(&sw[i16 * LD + 8 * g4]);
+      dk0 = mma_16x16x32(Sa, frag_col(b0, 32 * qb + 8 * g4, i16), dk0);
+      dk1 = mma_16x16x32(Sa, frag_col(b0, 32 * qb + 8 * g4, 16 + i16), dk1);
+      asm volatile("" ::: "memory");
     }
-    float* dkg = p.dqkv + (base + j) * 3 * C + C + h * D;
 #pragma unroll
-    for (int e = 0; e < D; e += 4) {
-      *reinterpret_cast<float4*>(dkg + e) = make_float4(dk[e], dk[e + 1], dk[e + 2], dk[e + 3]);
-      *reinterpret_cast<float4*>(dkg + C + e) = make_float4(dv[e], dv[e + 1], dv[e + 2], dv[e + 3]);
+    for (int r = 0; r < 4; ++r) {
+      const int k = k0 + 4 * g4 + r;
+      float a0 = c * dk0[r], a1 = c * dk1[r];
+      if constexpr (V2) {
+        const bool real = k < N;
+        const float* kr = qkv + (base + (real ? k : 0)) * 3 * C + C;
+        const float inv = 1.f / fmaxf(nk[k], p.eps);
+        const float h0 = real ? kr[i16] * inv : 0.f, h1 = real ? kr[16 + i16] * inv : 0.f;
+        float pr = h0 * a0 + h1 * a1;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) pr += __shfl_xor(pr, d);
+        const bool big = nk[k] > p.eps;
+        a0 = (big ? a0 - h0 * pr : a0) * inv;
+        a1 = (big ? a1 - h1 * pr : a1) * inv;
+      }
+      if (k < N) {
+        float* dg = p.dqkv + (base + k) * 3 * C + C + h * D;
+        dg[i16] = a0;
+        dg[16 + i16] = a1;
+        dg[C + i16] = dv0[r];
+        dg[C + 16 + i16] = dv1[r];
+      }
     }
   }
-  for (int e = t; e < R * R; e += NMAX) atomicAdd(p.dtable + (int64_t)e * g.heads + h, dtab[e]);
+  for (int e = t; e < R2; e += NP * 4) atomicAdd(p.dtable + (int64_t)e * g.heads + h, dtab[e]);
   if constexpr (V2) {
-    // d(t_eff) = -sum dS cos / t_eff^2, passed to tau where tau > tau_min.
     float v = dtau_acc;
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-    if ((t & 63) == 0) red[t >> 6] = v;
+    if (lane == 0) red[wave] = v;
     __syncthreads();
     if (t == 0 && p.tau[h] > p.tau_min) {
-      float s = 0.f;
-      for (int k = 0; k < NMAX / 64; ++k) s += red[k];
-      atomicAdd(p.dtau + h, -s / (t_eff * t_eff));
+      float sum = 0.f;
+      for (int k = 0; k < NWV; ++k) sum += red[k];
+      atomicAdd(p.dtau + h, -sum / (t_eff * t_eff));
     }
   }
+}
+
+template <int NP>
+void attn_bwd_launch(const AttnBwd& p, bool v2, int items, hipStream_t st) {
+  if (v2)
+    hipLaunchKernelGGL((attn_bwd_mfma_kernel<NP, true>), dim3(items), dim3(4 * NP), 0, st, p);
+  else
+    hipLaunchKernelGGL((attn_bwd_mfma_kernel<NP, false>), dim3(items), dim3(4 * NP), 0, st, p);
 }
 
 template <typename TA, typename TB, typename TC, bool ATOMIC>
@@ -524,13 +639,10 @@ hipError_t backward(const BwdArgs& a, hipStream_t st) {
   p.qkv = a.qkv; p.dout = a.dout; p.table = a.table; p.tau = a.tau;
   p.o = a.o; p.dqkv = a.dqkv; p.dtable = a.dtable; p.dtau = a.dtau;
   const int items = g.B * g.nW * g.heads;
-  if (g.N <= 64) {
-    if (a.v2) hipLaunchKernelGGL((attn_bwd_kernel<64, true>), dim3(items), dim3(64), 0, st, p);
-    else hipLaunchKernelGGL((attn_bwd_kernel<64, false>), dim3(items), dim3(64), 0, st, p);
-  } else {
-    if (a.v2) hipLaunchKernelGGL((attn_bwd_kernel<256, true>), dim3(items), dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((attn_bwd_kernel<256, false>), dim3(items), dim3(256), 0, st, p);
-  }
+if (g.N <= 32) attn_bwd_launch<32>(p, a.v2, items, st);
+  else if (g.N <= 64) attn_bwd_launch<64>(p, a.v2, items, st);
+  else if (g.N <= 128) attn_bwd_launch<128>(p, a.v2, items, st);
+  else attn_bwd_launch<256>(p, a.v2, items, st);
   TRY(hipGetLastError());
   // dWp = dyw^T o   [C, C];  dbp = colsum(dyw)
   BwdGemm wp{};

@@ -86,6 +86,8 @@ CASES = [
     (1, 32, 32, 64, 2, 16, 8, "bf16", "v2"),
     (1, 12, 12, 32, 1, 4, 2, "fp32", "v1"),     # window 4
     (1, 7, 7, 32, 1, 7, 3, "fp32", "v2"),       # window = image, shifted
+    (1, 20, 30, 64, 2, 10, 5, "fp32", "v1"),    # window 10: 100 tokens padded to 128
+    (2, 12, 12, 64, 2, 3, 1, "fp32", "v2"),     # window 3: 9 tokens padded to 32
 ]
 
 
