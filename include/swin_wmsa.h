@@ -245,6 +245,24 @@ typedef struct {
   float* dtau;     /* [heads]; V2 only (ignored and may be NULL in V1) */
 } swin_wmsa_grads;
 
+/*
+ * Backward of the V2 meta-network (same page and section as swin_cpb_table):
+ * given dtable = dL/dtable [(2M-1)^2, heads] (e.g. from swin_wmsa_bwd), writes
+ * dw1 [hidden, 2], db1 [hidden], dw2 [heads, hidden] and db2 [heads] (NULL
+ * allowed: then not written) for the table of swin_cpb_table with the same
+ * w1, b1, w2, b2, M and coord_scale.  Reading: ReLU'(0) = 0.  Every output is
+ * overwritten.  All float32; hidden in 1..4096, heads in 1..64, M in 1..32
+ * (else SWIN_ERR_SHAPE); workspace, ws_bytes >= swin_cpb_bwd_workspace_size
+ * (the sigmoid-side gradient, (2M-1)^2 x heads floats); no output may overlap
+ * an input, another output or the workspace (SWIN_ERR_ALIAS).
+ */
+size_t swin_cpb_bwd_workspace_size(int hidden, int heads, int M);
+
+swin_status swin_cpb_bwd(const float* w1, const float* b1, const float* w2, const float* b2,
+                         int hidden, int heads, int M, float coord_scale, const float* dtable,
+                         float* dw1, float* db1, float* dw2, float* db2, void* workspace,
+                         size_t ws_bytes, void* stream);
+
 /* Workspace bytes of swin_wmsa_bwd (0 for an invalid descriptor or B == 0). */
 size_t swin_wmsa_bwd_workspace_size(const swin_wmsa_desc* desc);
 

@@ -23,7 +23,7 @@ _EXPORTS = ("swin_status_str", "swin_abi_version", "swin_partition_shift", "swin
             "swin_cpb_table", "swin_wmsa_workspace_size", "swin_wmsa_fwd",
             "swin_wmsa_kernel_count", "swin_wmsa_kernel_name", "swin_wmsa_fwd_timed",
             "swin_block_workspace_size", "swin_block_fwd", "swin_wmsa_bwd_workspace_size",
-            "swin_wmsa_bwd")
+            "swin_wmsa_bwd", "swin_cpb_bwd_workspace_size", "swin_cpb_bwd")
 
 
 class SwinDesc(ctypes.Structure):
@@ -93,6 +93,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swin_wmsa_bwd.restype = st
     lib.swin_wmsa_bwd.argtypes = [ctypes.POINTER(SwinDesc), vp, vp, vp, vp, vp, vp, vp,
                                   ctypes.POINTER(Grads), vp, ctypes.c_size_t, vp]
+    lib.swin_cpb_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.swin_cpb_bwd_workspace_size.argtypes = [i, i, i]
+    lib.swin_cpb_bwd.restype = st
+    lib.swin_cpb_bwd.argtypes = [vp, vp, vp, vp, i, i, i, f, vp, vp, vp, vp, vp, vp,
+                                 ctypes.c_size_t, vp]
     _lib = lib
     return lib
 
@@ -234,6 +239,24 @@ def wmsa_bwd(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv: Optional[torch.Tensor]
         _ptr(tau), _ptr(dy), ctypes.byref(g), _ptr(workspace), workspace.numel(),
         _stream(stream)))
     return grads
+
+
+def cpb_bwd(w1, b1, w2, b2, M: int, dtable: torch.Tensor, coord_scale: float = 0.0,
+            stream=None) -> dict:
+    """Gradients of the V2 meta-network parameters for dL/dtable: dw1, db1, dw2,
+    db2 (float32)."""
+    hidden, heads = w1.shape[0], w2.shape[0]
+    f = dict(dtype=torch.float32, device=w1.device)
+    out = {"dw1": torch.empty(hidden, 2, **f), "db1": torch.empty(hidden, **f),
+           "dw2": torch.empty(heads, hidden, **f), "db2": torch.empty(heads, **f)}
+    lib = load_library()
+    ws = torch.empty(max(int(lib.swin_cpb_bwd_workspace_size(hidden, heads, M)), 1),
+                     dtype=torch.uint8, device=w1.device)
+    _check(lib.swin_cpb_bwd(_ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), hidden, heads, M,
+                            float(coord_scale), _ptr(dtable), _ptr(out["dw1"]), _ptr(out["db1"]),
+                            _ptr(out["dw2"]), _ptr(out["db2"]), _ptr(ws), ws.numel(),
+                            _stream(stream)))
+    return out
 
 
 def make_block_desc(B, H, W, C, heads, M, s, mode="v1", dtype=torch.bfloat16, hidden=None,

@@ -411,3 +411,34 @@ swin_status swin_wmsa_bwd(const swin_wmsa_desc* d, const void* x, const void* w_
   }
   return from_hip(launch_backward(a, static_cast<hipStream_t>(stream)));
 }
+
+size_t swin_cpb_bwd_workspace_size(int hidden, int heads, int M) {
+  if (hidden < 1 || hidden > 4096 || heads < 1 || heads > 64 || M < 1 || M > 32) return 0;
+  return round_up((size_t)(2 * M - 1) * (2 * M - 1) * heads * sizeof(float), 256);
+}
+
+swin_status swin_cpb_bwd(const float* w1, const float* b1, const float* w2, const float* b2,
+                         int hidden, int heads, int M, float coord_scale, const float* dtable,
+                         float* dw1, float* db1, float* dw2, float* db2, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  if (!w1 || !b1 || !w2 || !dtable || !dw1 || !db1 || !dw2 || !workspace) return SWIN_ERR_NULL;
+  const size_t ws = swin_cpb_bwd_workspace_size(hidden, heads, M);
+  if (ws == 0) return SWIN_ERR_SHAPE;
+  if (ws_bytes < ws) return SWIN_ERR_WORKSPACE;
+  const size_t tb = (size_t)(2 * M - 1) * (2 * M - 1) * heads * 4, hb = (size_t)hidden * 4;
+  struct Span { const void* p; size_t n; };
+  const Span outs[] = {{dw1, 2 * hb}, {db1, hb}, {dw2, heads * hb}, {db2, heads * 4u},
+                       {workspace, ws}};
+  const Span ins[] = {{w1, 2 * hb}, {b1, hb}, {w2, heads * hb}, {b2, heads * 4u}, {dtable, tb}};
+  const int no = sizeof(outs) / sizeof(outs[0]), ni = sizeof(ins) / sizeof(ins[0]);
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j)
+      if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return SWIN_ERR_ALIAS;
+    for (int j = i + 1; j < no; ++j)
+      if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return SWIN_ERR_ALIAS;
+  }
+  if (!(coord_scale > 0.0f)) coord_scale = M > 1 ? 8.0f / (float)(M - 1) : 1.0f;
+  return from_hip(launch_cpb_bwd(w1, b1, w2, b2, hidden, heads, M, coord_scale, dtable, dw1, db1,
+                                 dw2, db2, static_cast<float*>(workspace),
+                                 static_cast<hipStream_t>(stream)));
+}

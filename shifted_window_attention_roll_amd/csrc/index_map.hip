@@ -70,6 +70,17 @@ hipError_t launch_reverse_unshift(const void* xw, void* x, const Geom& g, int el
 // One block per relative offset row; the hidden layer goes through LDS and each
 // wave reduces whole heads.
 // ---------------------------------------------------------------------------
+// Log-spaced meta-network input of table row `row`: u = coord_scale * (dy,
+// dx), g(u) = sign(u) log2(1 + |u|) / log2(8) per component.
+__device__ __forceinline__ void cpb_coords(int row, int M, float coord_scale, float& gy,
+                                           float& gx) {
+  const int n = 2 * M - 1;
+  const float dy = (float)(row / n - (M - 1)) * coord_scale;
+  const float dx = (float)(row % n - (M - 1)) * coord_scale;
+  gy = copysignf(log2f(1.0f + fabsf(dy)) * (1.0f / 3.0f), dy);
+  gx = copysignf(log2f(1.0f + fabsf(dx)) * (1.0f / 3.0f), dx);
+}
+
 __global__ __launch_bounds__(256) void cpb_table_kernel(const float* __restrict__ w1,
                                                         const float* __restrict__ b1,
                                                         const float* __restrict__ w2,
@@ -78,12 +89,8 @@ __global__ __launch_bounds__(256) void cpb_table_kernel(const float* __restrict_
                                                         float* __restrict__ table) {
   extern __shared__ float hid[];
   const int row = blockIdx.x;
-  const int n = 2 * M - 1;
-  const float dy = (float)(row / n - (M - 1)) * coord_scale;
-  const float dx = (float)(row % n - (M - 1)) * coord_scale;
-  // g(u) = sign(u) log2(1 + |u|) / log2(8)
-  const float gy = copysignf(log2f(1.0f + fabsf(dy)) * (1.0f / 3.0f), dy);
-  const float gx = copysignf(log2f(1.0f + fabsf(dx)) * (1.0f / 3.0f), dx);
+  float gy, gx;
+  cpb_coords(row, M, coord_scale, gy, gx);
   for (int i = threadIdx.x; i < hidden; i += blockDim.x) {
     float h = fmaf(w1[2 * i], gy, fmaf(w1[2 * i + 1], gx, b1[i]));
     hid[i] = h > 0.0f ? h : 0.0f;
@@ -100,6 +107,125 @@ __global__ __launch_bounds__(256) void cpb_table_kernel(const float* __restrict_
       table[(int64_t)row * heads + hd] = 16.0f / (1.0f + expf(-o));
     }
   }
+}
+
+// Backward of the meta-network.  Pass 1, one workgroup per table row r:
+// dO[r, h] = dtable[r, h] * 16 sigmoid'(o[r, h]) (o the pre-sigmoid output).
+__global__ __launch_bounds__(256) void cpb_bwd_out_kernel(const float* __restrict__ w1,
+                                                          const float* __restrict__ b1,
+                                                          const float* __restrict__ w2,
+                                                          const float* __restrict__ b2,
+                                                          int hidden, int heads, int M,
+                                                          float coord_scale,
+                                                          const float* __restrict__ dtable,
+                                                          float* __restrict__ dout) {
+  extern __shared__ float hid[];
+  const int row = blockIdx.x;
+  float gy, gx;
+  cpb_coords(row, M, coord_scale, gy, gx);
+  for (int i = threadIdx.x; i < hidden; i += blockDim.x) {
+    const float h = fmaf(w1[2 * i], gy, fmaf(w1[2 * i + 1], gx, b1[i]));
+    hid[i] = h > 0.0f ? h : 0.0f;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int hd = wave; hd < heads; hd += blockDim.x >> 6) {
+    float acc = 0.0f;
+    for (int i = lane; i < hidden; i += 64) acc = fmaf(w2[(int64_t)hd * hidden + i], hid[i], acc);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) {
+      const float sg = 1.0f / (1.0f + expf(-(acc + (b2 ? b2[hd] : 0.0f))));
+      dout[(int64_t)row * heads + hd] = dtable[(int64_t)row * heads + hd] * 16.0f * sg * (1.0f - sg);
+    }
+  }
+}
+
+// Pass 2, one thread per hidden unit i (rows r in LDS chunks of dO):
+//   dw2[h, i] = sum_r dO[r, h] relu(pre[r, i]);
+//   dpre[r, i] = (sum_h dO[r, h] w2[h, i]) [pre[r, i] > 0];
+//   dw1[i, :] = sum_r dpre[r, i] g[r],  db1[i] = sum_r dpre[r, i];
+// and thread h < heads also db2[h] = sum_r dO[r, h].  Every output element is
+// written by one thread (no accumulation across calls).
+constexpr int kCpbHeads = 64, kCpbChunk = 64;
+
+__global__ __launch_bounds__(256) void cpb_bwd_param_kernel(const float* __restrict__ w1,
+                                                            const float* __restrict__ b1,
+                                                            const float* __restrict__ w2,
+                                                            int hidden, int heads, int M,
+                                                            float coord_scale,
+                                                            const float* __restrict__ dout,
+                                                            float* __restrict__ dw1,
+                                                            float* __restrict__ db1,
+                                                            float* __restrict__ dw2,
+                                                            float* __restrict__ db2) {
+  __shared__ float dsh[kCpbChunk][kCpbHeads];
+  __shared__ float gsh[kCpbChunk][2];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const bool live = i < hidden;
+  const int rows = (2 * M - 1) * (2 * M - 1);
+  float wa = 0.f, wb = 0.f, bb = 0.f, w2c[kCpbHeads];
+#pragma unroll
+  for (int hd = 0; hd < kCpbHeads; ++hd) w2c[hd] = (live && hd < heads) ? w2[(int64_t)hd * hidden + i] : 0.f;
+  if (live) {
+    wa = w1[2 * i];
+    wb = w1[2 * i + 1];
+    bb = b1[i];
+  }
+  float a2[kCpbHeads] = {};
+  float g0 = 0.f, g1 = 0.f, gb = 0.f, d2 = 0.f;
+  for (int r0 = 0; r0 < rows; r0 += kCpbChunk) {
+    const int nr = min(kCpbChunk, rows - r0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < nr * kCpbHeads; e += 256) {
+      const int rr = e / kCpbHeads, hd = e - rr * kCpbHeads;
+      dsh[rr][hd] = hd < heads ? dout[(int64_t)(r0 + rr) * heads + hd] : 0.f;
+    }
+    for (int rr = threadIdx.x; rr < nr; rr += 256) cpb_coords(r0 + rr, M, coord_scale, gsh[rr][0], gsh[rr][1]);
+    __syncthreads();
+    for (int rr = 0; rr < nr; ++rr) {
+      const float gy = gsh[rr][0], gx = gsh[rr][1];
+      const float pre = fmaf(wa, gy, fmaf(wb, gx, bb));
+      const float hv = pre > 0.f ? pre : 0.f;
+      float dp = 0.f;
+#pragma unroll
+      for (int hd = 0; hd < kCpbHeads; ++hd) {
+        const float d = dsh[rr][hd];
+        a2[hd] = fmaf(d, hv, a2[hd]);
+        dp = fmaf(d, w2c[hd], dp);
+      }
+      if (pre > 0.f) {
+        g0 = fmaf(dp, gy, g0);
+        g1 = fmaf(dp, gx, g1);
+        gb += dp;
+      }
+      if (threadIdx.x + blockIdx.x * 256 < heads) d2 += dsh[rr][threadIdx.x];
+    }
+  }
+  if (live) {
+#pragma unroll
+    for (int hd = 0; hd < kCpbHeads; ++hd)
+      if (hd < heads) dw2[(int64_t)hd * hidden + i] = a2[hd];
+    dw1[2 * i] = g0;
+    dw1[2 * i + 1] = g1;
+    db1[i] = gb;
+  }
+  if (db2 && blockIdx.x == 0 && threadIdx.x < heads) db2[threadIdx.x] = d2;
+}
+
+hipError_t launch_cpb_bwd(const float* w1, const float* b1, const float* w2, const float* b2,
+                          int hidden, int heads, int M, float coord_scale, const float* dtable,
+                          float* dw1, float* db1, float* dw2, float* db2, float* dout,
+                          hipStream_t st) {
+  if (heads > kCpbHeads) return hipErrorInvalidValue;
+  const int rows = (2 * M - 1) * (2 * M - 1);
+  hipLaunchKernelGGL(cpb_bwd_out_kernel, dim3(rows), dim3(256), hidden * sizeof(float), st, w1,
+                     b1, w2, b2, hidden, heads, M, coord_scale, dtable, dout);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cpb_bwd_param_kernel, dim3((hidden + 255) / 256), dim3(256), 0, st, w1, b1,
+                     w2, hidden, heads, M, coord_scale, dout, dw1, db1, dw2, db2);
+  return hipGetLastError();
 }
 
 hipError_t launch_cpb_table(const float* w1, const float* b1, const float* w2, const float* b2,

@@ -46,6 +46,10 @@ hipError_t launch_reverse_unshift(const void* xw, void* x, const Geom& g, int el
 hipError_t launch_cpb_table(const float* w1, const float* b1, const float* w2, const float* b2,
                             int hidden, int heads, int M, float coord_scale, float* table,
                             hipStream_t st);
+hipError_t launch_cpb_bwd(const float* w1, const float* b1, const float* w2, const float* b2,
+                          int hidden, int heads, int M, float coord_scale, const float* dtable,
+                          float* dw1, float* db1, float* dw2, float* db2, float* dout,
+                          hipStream_t st);
 hipError_t launch_qkv_gemm(const FwdParams& p, hipStream_t st);
 hipError_t launch_window_attn(const FwdParams& p, hipStream_t st);
 hipError_t launch_proj_gemm(const FwdParams& p, hipStream_t st);

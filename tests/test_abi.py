@@ -248,3 +248,24 @@ def test_bwd_rejects_before_launch(lib):
     assert _bwd(lib, d, ws=FAKE * 64 + 8) == ALIGN
     assert lib.swin_wmsa_bwd(None, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE, 0,
                              None) == NULL
+
+
+def test_cpb_bwd_rejects_before_launch(lib):
+    assert lib.swin_cpb_bwd_workspace_size(512, 16, 24) == ((47 * 47 * 16 * 4 + 255) // 256) * 256
+    assert lib.swin_cpb_bwd_workspace_size(512, 65, 24) == 0
+    F = FAKE
+
+    def call(**kw):
+        a = dict(w1=F, b1=F * 2, w2=F * 3, b2=F * 4, hidden=512, heads=16, M=24, dt=F * 5,
+                 dw1=F * 8, db1=F * 9, dw2=F * 10, db2=F * 11, ws=F * 12, wsb=1 << 20)
+        a.update(kw)
+        return lib.swin_cpb_bwd(a["w1"], a["b1"], a["w2"], a["b2"], a["hidden"], a["heads"],
+                                a["M"], 0.0, a["dt"], a["dw1"], a["db1"], a["dw2"], a["db2"],
+                                a["ws"], a["wsb"], None)
+    assert call(w1=None) == NULL
+    assert call(ws=None) == NULL
+    assert call(heads=0) == SHAPE
+    assert call(M=33) == SHAPE
+    assert call(wsb=16) == WS
+    assert call(dw2=F * 3 + 4) == ALIAS          # output over an input
+    assert call(db1=F * 8 + 4) == ALIAS          # two outputs overlap

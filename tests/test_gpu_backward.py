@@ -147,3 +147,27 @@ def test_backward_deterministic_except_atomics(gpu):
     for k in ("dw_qkv", "dw_proj", "dtable"):
         scale = float(a[k].abs().max())
         torch.testing.assert_close(a[k], b[k], rtol=0, atol=1e-6 * scale)
+
+
+@pytest.mark.parametrize("M,hidden,heads", [(8, 512, 4), (16, 256, 3), (24, 512, 16), (3, 64, 1)])
+def test_cpb_backward(gpu, M, hidden, heads):
+    # Meta-network backward against the oracle's, for a seeded table gradient.
+    _say(f"cpb bwd M={M} hidden={hidden} heads={heads}")
+    case = workloads.make_case(1, M, M, 32 * heads, heads, M, (0,), "bf16", "v2", seed=M + hidden,
+                               cpb_hidden=hidden)
+    blk = case.blocks[0]
+    dt = workloads.make_upstream_grad(((2 * M - 1) ** 2, heads), "fp32", M * 7)
+    dev = "cuda"
+    got = gpu.cpb_bwd(blk.cpb_w1.to(dev), blk.cpb_b1.to(dev), blk.cpb_w2.to(dev),
+                      blk.cpb_b2.to(dev), M, dt.to(dev))
+    torch.cuda.synchronize()
+    ref = sbw.cpb_backward(workloads.f64(blk.cpb_w1), workloads.f64(blk.cpb_b1),
+                           workloads.f64(blk.cpb_w2), workloads.f64(blk.cpb_b2), M,
+                           workloads.f64(dt))
+    for k in ("dw1", "db1", "dw2", "db2"):
+        g = workloads.f64(got[k].cpu())
+        r = ref[k]
+        scale = max(float(np.abs(r).max()), 1e-30)
+        err = float(np.abs(g - r).max())
+        _say(f"  {k}: max err {err:.3g} (scale {scale:.3g})")
+        assert err <= TOL * scale, (k, err, scale)
