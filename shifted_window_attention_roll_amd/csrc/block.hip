@@ -205,6 +205,125 @@ hipError_t launch_ln(const T* a, const T* b, T* u, const T* g, const T* be, cons
   return hipGetLastError();
 }
 
+// The whole MLP of a token row in one kernel, for 16-bit I/O and C <= 128:
+// y = GELU(a W1^T + b1) W2^T + b2 (+ r), the hidden layer never leaving the
+// chip.  Each wave owns RT tiles of 16 rows; per 32 hidden units it computes
+// the hidden tile on the matrix cores (A = the rows' fragments, kept in
+// registers; B = W1 rows), applies bias and the exact GELU, rounds it to the
+// I/O type (the rounding an unfused MLP stores), passes it through a per-wave
+// LDS tile to become row fragments, and accumulates Y += H W2^T (B = W2 rows,
+// contiguous in the hidden index).  Weights are read from L2; each fragment
+// serves the wave's RT row tiles.
+constexpr int kMlpRT = 2, kMlpLD = 40;
+
+template <typename T, int C, bool RES>
+__global__ __launch_bounds__(256) void mlp_fused_kernel(const T* __restrict__ a,
+                                                        const T* __restrict__ w1,
+                                                        const T* __restrict__ b1,
+                                                        const T* __restrict__ w2,
+                                                        const T* __restrict__ b2,
+                                                        const T* __restrict__ r, T* __restrict__ y,
+                                                        int rows, int hidden) {
+  constexpr int KC = C / 32, CT = C / 16, RT = kMlpRT;
+  __shared__ __attribute__((aligned(16))) T hs[4][RT][16 * kMlpLD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * 16 * RT;
+  vec8<T> xa[RT][KC];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t ra = r0 + 16 * rt + i16;
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      if (ra < rows) {
+        xa[rt][kk] = gload8(a + ra * C + 32 * kk + 8 * g4);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xa[rt][kk][e] = from_f32<T>(0.f);
+      }
+    }
+  }
+  f32x4 yacc[RT][CT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) yacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hc = 0; hc < hidden; hc += 32) {
+    // Hidden tile [16 rows][32 units] per row tile: 2 products of 16 columns.
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int n = hc + 16 * t + i16;  // this lane's hidden unit (B column)
+      vec8<T> wb[KC];
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) wb[kk] = gload8(w1 + (int64_t)n * C + 32 * kk + 8 * g4);
+      const float bn = b1 ? (float)b1[n] : 0.f;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 h = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) h = mma_16x16x32(xa[rt][kk], wb[kk], h);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v = h[q] + bn;
+          hs[wave][rt][(4 * g4 + q) * kMlpLD + 16 * t + i16] =
+              from_f32<T>(0.5f * v * (1.0f + erff(v * 0.70710678118654752f)));
+        }
+      }
+    }
+    asm volatile("" ::: "memory");  // the wave's tile writes before its reads
+    vec8<T> wb2[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      wb2[ct] = gload8(w2 + (int64_t)(16 * ct + i16) * hidden + hc + 8 * g4);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const vec8<T> ha = load8(&hs[wave][rt][i16 * kMlpLD + 8 * g4]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) yacc[rt][ct] = mma_16x16x32(ha, wb2[ct], yacc[rt][ct]);
+    }
+    asm volatile("" ::: "memory");  // reads done before the next chunk's writes
+  }
+  // Lane: channel 16 ct + i16 of rows 4 g4 + q of each row tile.
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int c = 16 * ct + i16;
+    const float bc = b2 ? (float)b2[c] : 0.f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = r0 + 16 * rt + 4 * g4 + q;
+        if (row >= rows) continue;
+        float v = yacc[rt][ct][q] + bc;
+        if constexpr (RES) v += (float)r[row * C + c];
+        y[row * C + c] = from_f32<T>(v);
+      }
+  }
+}
+
+template <typename T, bool RES>
+hipError_t launch_mlp_fused(const T* A, const T* w1, const T* b1, const T* w2, const T* b2,
+                            const T* R, T* Y, int rows, int C, int hidden, hipStream_t st) {
+  if constexpr (__is_same(T, float)) {
+    return hipErrorInvalidValue;  // 16-bit operands only
+  } else {
+  const int per_wg = 4 * 16 * kMlpRT;
+  const dim3 grid((rows + per_wg - 1) / per_wg), block(256);
+  switch (C) {
+    case 32: hipLaunchKernelGGL((mlp_fused_kernel<T, 32, RES>), grid, block, 0, st, A, w1, b1, w2, b2, R, Y, rows, hidden); break;
+    case 64: hipLaunchKernelGGL((mlp_fused_kernel<T, 64, RES>), grid, block, 0, st, A, w1, b1, w2, b2, R, Y, rows, hidden); break;
+    case 96: hipLaunchKernelGGL((mlp_fused_kernel<T, 96, RES>), grid, block, 0, st, A, w1, b1, w2, b2, R, Y, rows, hidden); break;
+    case 128: hipLaunchKernelGGL((mlp_fused_kernel<T, 128, RES>), grid, block, 0, st, A, w1, b1, w2, b2, R, Y, rows, hidden); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+  }
+}
+
+bool mlp_fused_supported(int C, int io) {
+  return io != kF32 && C % 32 == 0 && C <= 128;
+}
+
 template <typename T, bool GELU, bool RES>
 hipError_t launch_dense(const T* A, const T* Wt, const T* bias, const T* R, T* Y, int rows, int N,
                         int K, hipStream_t st) {
@@ -272,6 +391,8 @@ swin_status block_run(const swin_block_desc* d, const T* x, const swin_block_par
   T* U = reinterpret_cast<T*>(ws + L.u);
   auto P = [](const void* q) { return static_cast<const T*>(q); };
   const size_t attn_ws = L.a;  // the attention's workspace is the first region
+  constexpr int io = __is_same(T, float) ? kF32 : __is_same(T, h16) ? kF16 : kBF16;
+  const bool fused_mlp = mlp_fused_supported(C, io);
   swin_status s;
   hipError_t e;
   if (at.mode == SWIN_V1) {
@@ -281,6 +402,9 @@ swin_status block_run(const swin_block_desc* d, const T* x, const swin_block_par
                       attn_ws ? ws : nullptr, attn_ws, st);
     if (s != SWIN_OK) return s;
     e = launch_ln<T>(x, Bv, Hb, P(p->ln2_g), P(p->ln2_b), nullptr, A, rows, C, eps, st);
+    if (e == hipSuccess && fused_mlp)
+      return hip_status(launch_mlp_fused<T, true>(A, P(p->fc1_w), P(p->fc1_b), P(p->fc2_w),
+                                                  P(p->fc2_b), Hb, y, rows, C, hid, st));
     if (e == hipSuccess)
       e = launch_dense<T, true, false>(A, P(p->fc1_w), P(p->fc1_b), nullptr, U, rows, hid, C, st);
     if (e == hipSuccess)
@@ -291,10 +415,15 @@ swin_status block_run(const swin_block_desc* d, const T* x, const swin_block_par
                     attn_ws ? ws : nullptr, attn_ws, st);
   if (s != SWIN_OK) return s;
   e = launch_ln<T>(Bv, nullptr, nullptr, P(p->ln1_g), P(p->ln1_b), x, Hb, rows, C, eps, st);
-  if (e == hipSuccess)
-    e = launch_dense<T, true, false>(Hb, P(p->fc1_w), P(p->fc1_b), nullptr, U, rows, hid, C, st);
-  if (e == hipSuccess)
-    e = launch_dense<T, false, false>(U, P(p->fc2_w), P(p->fc2_b), nullptr, A, rows, C, hid, st);
+  if (e == hipSuccess && fused_mlp) {
+    e = launch_mlp_fused<T, false>(Hb, P(p->fc1_w), P(p->fc1_b), P(p->fc2_w), P(p->fc2_b),
+                                   nullptr, A, rows, C, hid, st);
+  } else {
+    if (e == hipSuccess)
+      e = launch_dense<T, true, false>(Hb, P(p->fc1_w), P(p->fc1_b), nullptr, U, rows, hid, C, st);
+    if (e == hipSuccess)
+      e = launch_dense<T, false, false>(U, P(p->fc2_w), P(p->fc2_b), nullptr, A, rows, C, hid, st);
+  }
   if (e == hipSuccess)
     e = launch_ln<T>(A, nullptr, nullptr, P(p->ln2_g), P(p->ln2_b), Hb, y, rows, C, eps, st);
   (void)ws_bytes;

@@ -88,6 +88,8 @@ def _setup(B, H, W, C, heads, M, s, dtype, mode, seed):
     (1, 14, 14, 512, 16, 7, 3, "bf16", "v1"),   # C = 512: 8 channels per lane in LayerNorm
     (1, 14, 14, 512, 16, 7, 3, "fp32", "v1"),   # hidden 2048: long K in float32
     (1, 16, 24, 256, 8, 8, 3, "fp16", "v2"),    # tiled attention between the GEMMs
+    (1, 10, 10, 64, 2, 5, 2, "bf16", "v1"),     # fused MLP, C = 64, 100 rows (ragged)
+    (3, 7, 7, 32, 1, 7, 3, "fp16", "v2"),       # fused MLP, C = 32, 147 rows
 ])
 def test_block_small(gpu, B, H, W, C, heads, M, s, dtype, mode):
     _say(f"block B={B} H={H} W={W} C={C} heads={heads} M={M} s={s} {dtype} {mode}")
