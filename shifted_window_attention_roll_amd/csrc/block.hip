@@ -205,42 +205,85 @@ hipError_t launch_ln(const T* a, const T* b, T* u, const T* g, const T* be, cons
   return hipGetLastError();
 }
 
-// The whole MLP of a token row in one kernel, for 16-bit I/O and C <= 128:
-// y = GELU(a W1^T + b1) W2^T + b2 (+ r), the hidden layer never leaving the
-// chip.  Each wave owns RT tiles of 16 rows; per 32 hidden units it computes
-// the hidden tile on the matrix cores (A = the rows' fragments, kept in
-// registers; B = W1 rows), applies bias and the exact GELU, rounds it to the
-// I/O type (the rounding an unfused MLP stores), passes it through a per-wave
-// LDS tile to become row fragments, and accumulates Y += H W2^T (B = W2 rows,
-// contiguous in the hidden index).  Weights are read from L2; each fragment
-// serves the wave's RT row tiles.
+// The whole MLP sub-layer of a token row in one kernel, for 16-bit I/O and
+// C <= 128, with the block's second LayerNorm and residual folded in:
+//   V1 (pre-norm):  h = a + a2,  y = h + F(LN(h));
+//   V2 (post-norm): h = a,       y = h + LN(F(h));
+// F(u) = GELU(u W1^T + b1) W2^T + b2.  Each wave owns RT tiles of 16 rows.
+// Their A fragments (row l % 16, channels 32 kk + 8 (l/16) .. +7) are loaded
+// once (V1: h, its LayerNorm across the four lanes of a row, rounded to the
+// I/O type as a stored LayerNorm output would be).  Per 32 hidden units: the
+// hidden tile on the matrix cores (B = W1 rows), bias, exact GELU, rounded to
+// the I/O type (the rounding an unfused MLP stores), through a per-wave LDS
+// tile to become row fragments, then Y += H W2^T (B = W2 rows, contiguous in
+// the hidden index).  Weights come from L2; each fragment serves the wave's
+// RT row tiles.  The hidden layer never reaches HBM.
 constexpr int kMlpRT = 2, kMlpLD = 40;
 
-template <typename T, int C, bool RES>
-__global__ __launch_bounds__(256) void mlp_fused_kernel(const T* __restrict__ a,
-                                                        const T* __restrict__ w1,
-                                                        const T* __restrict__ b1,
-                                                        const T* __restrict__ w2,
-                                                        const T* __restrict__ b2,
-                                                        const T* __restrict__ r, T* __restrict__ y,
-                                                        int rows, int hidden) {
+template <typename T>
+struct MlpArgs {
+  const T *a, *a2;     // h = a (+ a2)
+  const T *g, *be;     // the second LayerNorm's gamma, beta
+  const T *w1, *b1, *w2, *b2;
+  T* y;
+  int rows, hidden;
+  float eps;
+};
+
+template <typename T, int C, bool V1>
+__global__ __launch_bounds__(256) void mlp_fused_kernel(MlpArgs<T> p) {
   constexpr int KC = C / 32, CT = C / 16, RT = kMlpRT;
   __shared__ __attribute__((aligned(16))) T hs[4][RT][16 * kMlpLD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g4 = lane >> 4;
   const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * 16 * RT;
+  const int rows = p.rows, hidden = p.hidden;
   vec8<T> xa[RT][KC];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t ra = r0 + 16 * rt + i16;
+    const bool live = ra < rows;
+    float v[KC][8];
+    float sum = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
-      if (ra < rows) {
-        xa[rt][kk] = gload8(a + ra * C + 32 * kk + 8 * g4);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xa[rt][kk][e] = from_f32<T>(0.f);
+      const int c0 = 32 * kk + 8 * g4;
+      vec8<T> av = {}, bv = {};
+      if (live) {
+        av = gload8(p.a + ra * C + c0);
+        if constexpr (V1) bv = gload8(p.a2 + ra * C + c0);
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[kk][e] = (float)av[e] + (V1 ? (float)bv[e] : 0.f);
+        sum += v[kk][e];
+      }
+    }
+    if constexpr (V1) {
+      // LayerNorm over the row's C channels, spread over lanes l, l^16, l^32, l^48.
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      const float mean = sum / (float)C;
+      float q = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q += (v[kk][e] - mean) * (v[kk][e] - mean);
+      q += __shfl_xor(q, 16);
+      q += __shfl_xor(q, 32);
+      const float rstd = 1.0f / sqrtf(q / (float)C + p.eps);
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) {
+        const vec8<T> gv = gload8(p.g + 32 * kk + 8 * g4), be = gload8(p.be + 32 * kk + 8 * g4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          xa[rt][kk][e] = from_f32<T>((v[kk][e] - mean) * rstd * (float)gv[e] + (float)be[e]);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xa[rt][kk][e] = from_f32<T>(v[kk][e]);
     }
   }
   f32x4 yacc[RT][CT];
@@ -249,14 +292,13 @@ __global__ __launch_bounds__(256) void mlp_fused_kernel(const T* __restrict__ a,
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) yacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int hc = 0; hc < hidden; hc += 32) {
-    // Hidden tile [16 rows][32 units] per row tile: 2 products of 16 columns.
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int n = hc + 16 * t + i16;  // this lane's hidden unit (B column)
       vec8<T> wb[KC];
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) wb[kk] = gload8(w1 + (int64_t)n * C + 32 * kk + 8 * g4);
-      const float bn = b1 ? (float)b1[n] : 0.f;
+      for (int kk = 0; kk < KC; ++kk) wb[kk] = gload8(p.w1 + (int64_t)n * C + 32 * kk + 8 * g4);
+      const float bn = p.b1 ? (float)p.b1[n] : 0.f;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         f32x4 h = {0.f, 0.f, 0.f, 0.f};
@@ -274,7 +316,7 @@ __global__ __launch_bounds__(256) void mlp_fused_kernel(const T* __restrict__ a,
     vec8<T> wb2[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-      wb2[ct] = gload8(w2 + (int64_t)(16 * ct + i16) * hidden + hc + 8 * g4);
+      wb2[ct] = gload8(p.w2 + (int64_t)(16 * ct + i16) * hidden + hc + 8 * g4);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const vec8<T> ha = load8(&hs[wave][rt][i16 * kMlpLD + 8 * g4]);
@@ -284,39 +326,72 @@ __global__ __launch_bounds__(256) void mlp_fused_kernel(const T* __restrict__ a,
     asm volatile("" ::: "memory");  // reads done before the next chunk's writes
   }
   // Lane: channel 16 ct + i16 of rows 4 g4 + q of each row tile.
+  float bc[CT], gc[CT], bec[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int c = 16 * ct + i16;
-    const float bc = b2 ? (float)b2[c] : 0.f;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t row = r0 + 16 * rt + 4 * g4 + q;
-        if (row >= rows) continue;
-        float v = yacc[rt][ct][q] + bc;
-        if constexpr (RES) v += (float)r[row * C + c];
-        y[row * C + c] = from_f32<T>(v);
-      }
+    bc[ct] = p.b2 ? (float)p.b2[c] : 0.f;
+    gc[ct] = V1 ? 0.f : (float)p.g[c];
+    bec[ct] = V1 ? 0.f : (float)p.be[c];
   }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = r0 + 16 * rt + 4 * g4 + q;
+      float f[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) f[ct] = yacc[rt][ct][q] + bc[ct];
+      if constexpr (!V1) {
+        // LayerNorm of F over the row's C channels: CT per lane, 16 lanes.
+        float sum = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) sum += f[ct];
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) sum += __shfl_xor(sum, d);
+        const float mean = sum / (float)C;
+        float var = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) var += (f[ct] - mean) * (f[ct] - mean);
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) var += __shfl_xor(var, d);
+        const float rstd = 1.0f / sqrtf(var / (float)C + p.eps);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) f[ct] = (f[ct] - mean) * rstd * gc[ct] + bec[ct];
+      }
+      if (row >= rows) continue;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int c = 16 * ct + i16;
+        float h = (float)p.a[row * C + c];
+        if constexpr (V1) h += (float)p.a2[row * C + c];
+        p.y[row * C + c] = from_f32<T>(h + f[ct]);
+      }
+    }
 }
 
-template <typename T, bool RES>
-hipError_t launch_mlp_fused(const T* A, const T* w1, const T* b1, const T* w2, const T* b2,
-                            const T* R, T* Y, int rows, int C, int hidden, hipStream_t st) {
+template <typename T>
+hipError_t launch_mlp_fused(const MlpArgs<T>& a, int C, bool v1, hipStream_t st) {
   if constexpr (__is_same(T, float)) {
     return hipErrorInvalidValue;  // 16-bit operands only
   } else {
-  const int per_wg = 4 * 16 * kMlpRT;
-  const dim3 grid((rows + per_wg - 1) / per_wg), block(256);
-  switch (C) {
-    case 32: hipLaunchKernelGGL((mlp_fused_kernel<T, 32, RES>), grid, block, 0, st, A, w1, b1, w2, b2, R, Y, rows, hidden); break;
-    case 64: hipLaunchKernelGGL((mlp_fused_kernel<T, 64, RES>), grid, block, 0, st, A, w1, b1, w2, b2, R, Y, rows, hidden); break;
-    case 96: hipLaunchKernelGGL((mlp_fused_kernel<T, 96, RES>), grid, block, 0, st, A, w1, b1, w2, b2, R, Y, rows, hidden); break;
-    case 128: hipLaunchKernelGGL((mlp_fused_kernel<T, 128, RES>), grid, block, 0, st, A, w1, b1, w2, b2, R, Y, rows, hidden); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+    const int per_wg = 4 * 16 * kMlpRT;
+    const dim3 grid((a.rows + per_wg - 1) / per_wg), block(256);
+    auto go = [&](auto cc) {
+      constexpr int CC = decltype(cc)::value;
+      if (v1)
+        hipLaunchKernelGGL((mlp_fused_kernel<T, CC, true>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((mlp_fused_kernel<T, CC, false>), grid, block, 0, st, a);
+    };
+    switch (C) {
+      case 32: go(std::integral_constant<int, 32>()); break;
+      case 64: go(std::integral_constant<int, 64>()); break;
+      case 96: go(std::integral_constant<int, 96>()); break;
+      case 128: go(std::integral_constant<int, 128>()); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
   }
 }
 
@@ -401,10 +476,12 @@ swin_status block_run(const swin_block_desc* d, const T* x, const swin_block_par
     s = swin_wmsa_fwd(&at, A, p->w_qkv, p->b_qkv, p->w_proj, p->b_proj, p->bias_table, p->tau, Bv,
                       attn_ws ? ws : nullptr, attn_ws, st);
     if (s != SWIN_OK) return s;
+    if (fused_mlp) {
+      const MlpArgs<T> m{x, Bv, P(p->ln2_g), P(p->ln2_b), P(p->fc1_w), P(p->fc1_b),
+                         P(p->fc2_w), P(p->fc2_b), y, rows, hid, eps};
+      return hip_status(launch_mlp_fused<T>(m, C, true, st));
+    }
     e = launch_ln<T>(x, Bv, Hb, P(p->ln2_g), P(p->ln2_b), nullptr, A, rows, C, eps, st);
-    if (e == hipSuccess && fused_mlp)
-      return hip_status(launch_mlp_fused<T, true>(A, P(p->fc1_w), P(p->fc1_b), P(p->fc2_w),
-                                                  P(p->fc2_b), Hb, y, rows, C, hid, st));
     if (e == hipSuccess)
       e = launch_dense<T, true, false>(A, P(p->fc1_w), P(p->fc1_b), nullptr, U, rows, hid, C, st);
     if (e == hipSuccess)
@@ -416,14 +493,14 @@ swin_status block_run(const swin_block_desc* d, const T* x, const swin_block_par
   if (s != SWIN_OK) return s;
   e = launch_ln<T>(Bv, nullptr, nullptr, P(p->ln1_g), P(p->ln1_b), x, Hb, rows, C, eps, st);
   if (e == hipSuccess && fused_mlp) {
-    e = launch_mlp_fused<T, false>(Hb, P(p->fc1_w), P(p->fc1_b), P(p->fc2_w), P(p->fc2_b),
-                                   nullptr, A, rows, C, hid, st);
-  } else {
-    if (e == hipSuccess)
-      e = launch_dense<T, true, false>(Hb, P(p->fc1_w), P(p->fc1_b), nullptr, U, rows, hid, C, st);
-    if (e == hipSuccess)
-      e = launch_dense<T, false, false>(U, P(p->fc2_w), P(p->fc2_b), nullptr, A, rows, C, hid, st);
+    const MlpArgs<T> m{Hb, nullptr, P(p->ln2_g), P(p->ln2_b), P(p->fc1_w), P(p->fc1_b),
+                       P(p->fc2_w), P(p->fc2_b), y, rows, hid, eps};
+    return hip_status(launch_mlp_fused<T>(m, C, false, st));
   }
+  if (e == hipSuccess)
+    e = launch_dense<T, true, false>(Hb, P(p->fc1_w), P(p->fc1_b), nullptr, U, rows, hid, C, st);
+  if (e == hipSuccess)
+    e = launch_dense<T, false, false>(U, P(p->fc2_w), P(p->fc2_b), nullptr, A, rows, C, hid, st);
   if (e == hipSuccess)
     e = launch_ln<T>(A, nullptr, nullptr, P(p->ln2_g), P(p->ln2_b), Hb, y, rows, C, eps, st);
   (void)ws_bytes;
