@@ -263,6 +263,37 @@ swin_status swin_cpb_bwd(const float* w1, const float* b1, const float* w2, cons
                          float* dw1, float* db1, float* dw2, float* db2, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/*
+ * FP8 linear layers for the QKV and projection GEMMs.
+ *   Page: "Boosting Swin Transformer Speed", Inference Optimization (those GEMMs
+ *   in 8 bits with per-channel scales; the MI355X's native 8-bit float takes
+ *   the place of 8-bit integers).
+ * Format: OCP FP8 E4M3 (exponent bias 7, 3 mantissa bits, largest finite 448,
+ * subnormals k * 2^-9).
+ *
+ * swin_fp8_quantize: per row r of x [rows, K] (dtype dt): amax = max |x[r]|,
+ * scales[r] = amax / 448 and inv = 448 / amax (1 and 1 when amax = 0), codes
+ * [rows, K] = E4M3(x * inv) to nearest, ties to even, after clamping to
+ * +-448, sign bit set when x * inv < 0; every step in float32.  For an
+ * activation the rows are tokens; for a weight [out, in] the rows are output
+ * channels.  rows >= 0, 1 <= K <= 65536 (else SWIN_ERR_SHAPE); x 16-byte
+ * aligned (SWIN_ERR_ALIGN); codes, scales must not overlap x or each other
+ * (SWIN_ERR_ALIAS).
+ *
+ * swin_fp8_linear: y [rows, N] (y_dt) = (dec(a) dec(w)^T) * sa[:, None] *
+ * sw[None, :] + bias[None, :] with a [rows, K] and w [N, K] codes, sa [rows],
+ * sw [N] from swin_fp8_quantize, bias [N] (bias_dt) or NULL; products
+ * accumulate in float32.  K a multiple of 32, N >= 1, rows >= 0 (else
+ * SWIN_ERR_SHAPE); a, w 16-byte aligned (SWIN_ERR_ALIGN); y must not overlap
+ * an input (SWIN_ERR_ALIAS).
+ */
+swin_status swin_fp8_quantize(const void* x, swin_dtype dt, int rows, int K,
+                              unsigned char* codes, float* scales, void* stream);
+
+swin_status swin_fp8_linear(const unsigned char* a, const float* sa, const unsigned char* w,
+                            const float* sw, const void* bias, swin_dtype bias_dt, void* y,
+                            swin_dtype y_dt, int rows, int N, int K, void* stream);
+
 /* Workspace bytes of swin_wmsa_bwd (0 for an invalid descriptor or B == 0). */
 size_t swin_wmsa_bwd_workspace_size(const swin_wmsa_desc* desc);
 

@@ -23,7 +23,8 @@ _EXPORTS = ("swin_status_str", "swin_abi_version", "swin_partition_shift", "swin
             "swin_cpb_table", "swin_wmsa_workspace_size", "swin_wmsa_fwd",
             "swin_wmsa_kernel_count", "swin_wmsa_kernel_name", "swin_wmsa_fwd_timed",
             "swin_block_workspace_size", "swin_block_fwd", "swin_wmsa_bwd_workspace_size",
-            "swin_wmsa_bwd", "swin_cpb_bwd_workspace_size", "swin_cpb_bwd")
+            "swin_wmsa_bwd", "swin_cpb_bwd_workspace_size", "swin_cpb_bwd",
+            "swin_fp8_quantize", "swin_fp8_linear")
 
 
 class SwinDesc(ctypes.Structure):
@@ -98,6 +99,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swin_cpb_bwd.restype = st
     lib.swin_cpb_bwd.argtypes = [vp, vp, vp, vp, i, i, i, f, vp, vp, vp, vp, vp, vp,
                                  ctypes.c_size_t, vp]
+    lib.swin_fp8_quantize.restype = st
+    lib.swin_fp8_quantize.argtypes = [vp, i, i, i, vp, vp, vp]
+    lib.swin_fp8_linear.restype = st
+    lib.swin_fp8_linear.argtypes = [vp, vp, vp, vp, vp, i, vp, i, i, i, i, vp]
     _lib = lib
     return lib
 
@@ -256,6 +261,31 @@ def cpb_bwd(w1, b1, w2, b2, M: int, dtable: torch.Tensor, coord_scale: float = 0
                             float(coord_scale), _ptr(dtable), _ptr(out["dw1"]), _ptr(out["db1"]),
                             _ptr(out["dw2"]), _ptr(out["db2"]), _ptr(ws), ws.numel(),
                             _stream(stream)))
+    return out
+
+
+def fp8_quantize(x: torch.Tensor, stream=None):
+    """Per-row E4M3 codes (uint8, shape of x) and float32 scales of a 2-D tensor."""
+    rows, K = x.shape
+    codes = torch.empty(rows, K, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(load_library().swin_fp8_quantize(_ptr(x), _DT[x.dtype], rows, K, _ptr(codes),
+                                            _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def fp8_linear(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: torch.Tensor,
+               bias: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = (dec(a) dec(w)^T) * sa[:, None] * sw[None, :] + bias."""
+    rows, K = a.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty(rows, N, dtype=out_dtype, device=a.device)
+    _check(load_library().swin_fp8_linear(
+        _ptr(a), _ptr(sa), _ptr(w), _ptr(sw), _ptr(bias),
+        _DT[bias.dtype] if bias is not None else 0, _ptr(out), _DT[out.dtype], rows, N, K,
+        _stream(stream)))
     return out
 
 

@@ -442,3 +442,42 @@ swin_status swin_cpb_bwd(const float* w1, const float* b1, const float* w2, cons
                                  dw2, db2, static_cast<float*>(workspace),
                                  static_cast<hipStream_t>(stream)));
 }
+
+// ---------------------------------------------------------------------------
+// FP8 linear layers.
+
+namespace {
+bool valid_dt(int dt) { return dt == SWIN_F32 || dt == SWIN_F16 || dt == SWIN_BF16; }
+int io_of(int dt) { return dt == SWIN_F32 ? kF32 : dt == SWIN_F16 ? kF16 : kBF16; }
+}  // namespace
+
+swin_status swin_fp8_quantize(const void* x, swin_dtype dt, int rows, int K,
+                              unsigned char* codes, float* scales, void* stream) {
+  if (!valid_dt(dt)) return SWIN_ERR_DTYPE;
+  if (rows < 0 || K < 1 || K > 65536) return SWIN_ERR_SHAPE;
+  if (rows == 0) return SWIN_OK;
+  if (!x || !codes || !scales) return SWIN_ERR_NULL;
+  const size_t xb = (size_t)rows * K * elem_bytes(dt), cb = (size_t)rows * K, sb = rows * 4u;
+  if (overlap(codes, cb, x, xb) || overlap(scales, sb, x, xb) || overlap(codes, cb, scales, sb))
+    return SWIN_ERR_ALIAS;
+  if (!aligned16(x)) return SWIN_ERR_ALIGN;
+  return from_hip(launch_fp8_quant(x, io_of(dt), rows, K, codes, scales,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+swin_status swin_fp8_linear(const unsigned char* a, const float* sa, const unsigned char* w,
+                            const float* sw, const void* bias, swin_dtype bias_dt, void* y,
+                            swin_dtype y_dt, int rows, int N, int K, void* stream) {
+  if (!valid_dt(y_dt) || (bias && !valid_dt(bias_dt))) return SWIN_ERR_DTYPE;
+  if (rows < 0 || N < 1 || K < 32 || K % 32 || K > 65536) return SWIN_ERR_SHAPE;
+  if (rows == 0) return SWIN_OK;
+  if (!a || !sa || !w || !sw || !y) return SWIN_ERR_NULL;
+  const size_t yb = (size_t)rows * N * elem_bytes(y_dt);
+  if (overlap(y, yb, a, (size_t)rows * K) || overlap(y, yb, w, (size_t)N * K) ||
+      overlap(y, yb, sa, rows * 4u) || overlap(y, yb, sw, N * 4u) ||
+      (bias && overlap(y, yb, bias, (size_t)N * elem_bytes(bias_dt))))
+    return SWIN_ERR_ALIAS;
+  if (!aligned16(a) || !aligned16(w)) return SWIN_ERR_ALIGN;
+  Fp8Linear p{a, sa, w, sw, bias, bias ? io_of(bias_dt) : kF32, y, rows, N, K};
+  return from_hip(launch_fp8_linear(p, io_of(y_dt), static_cast<hipStream_t>(stream)));
+}

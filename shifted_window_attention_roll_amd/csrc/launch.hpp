@@ -132,6 +132,27 @@ struct BwdArgs {
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st);
 
+// FP8 linear layers (fp8.hip).
+struct Fp8Linear {
+  const uint8_t* a;   // [rows, K] E4M3 codes
+  const float* sa;    // [rows]
+  const uint8_t* w;   // [N, K] E4M3 codes
+  const float* sw;    // [N]
+  const void* bias;   // [N] of bias_type, or null
+  int bias_type;
+  void* y;            // [rows, N]
+  int64_t rows;
+  int N, K;
+};
+__device__ __forceinline__ float ld_any(const void* p, int type, int i) {
+  if (type == kF32) return static_cast<const float*>(p)[i];
+  if (type == kF16) return (float)static_cast<const h16*>(p)[i];
+  return (float)static_cast<const b16*>(p)[i];
+}
+hipError_t launch_fp8_quant(const void* x, int io, int rows, int K, uint8_t* codes, float* scales,
+                            hipStream_t st);
+hipError_t launch_fp8_linear(const Fp8Linear& p, int out_io, hipStream_t st);
+
 inline int max_window(int io_bytes) { return io_bytes == 4 ? 16 : 24; }
 
 }  // namespace swin
