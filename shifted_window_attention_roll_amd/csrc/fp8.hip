@@ -112,6 +112,142 @@ __global__ __launch_bounds__(256) void fp8_linear_kernel(Fp8Linear p) {
   }
 }
 
+// The same product for K a multiple of 128 on the gfx950 16x16x128 8-bit
+// float products (unit block scales).  128 x 128 tile per workgroup of 4
+// waves (64 x 64 each, 16 accumulator tiles); K in steps of 128 through LDS
+// (rows padded to 144 bytes), the next step's 16-byte chunks loaded into
+// registers during the current step.  A lane's fragment is 32 consecutive
+// bytes of one row; A and W use the same placement, so each product pairs
+// equal k.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kF8T = 128, kF8K = 128, kF8P = 144;
+
+template <typename TO>
+__global__ __launch_bounds__(256) void fp8_linear_tiled_kernel(Fp8Linear p) {
+  __shared__ __attribute__((aligned(16))) uint8_t as[kF8T * kF8P];
+  __shared__ __attribute__((aligned(16))) uint8_t ws[kF8T * kF8P];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int64_t m0 = (int64_t)blockIdx.y * kF8T;
+  const int n0 = blockIdx.x * kF8T;
+  // Staging: chunk c = tid + 256 i (i < 4) is row c / 8, bytes 16 (c % 8).
+  uint4 ra[4], rw[4];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, cc = c & 7;
+      const int64_t m = m0 + row;
+      const int n = n0 + row;
+      ra[i] = m < p.rows ? *reinterpret_cast<const uint4*>(p.a + m * p.K + kb + 16 * cc)
+                         : uint4{0u, 0u, 0u, 0u};
+      rw[i] = n < p.N ? *reinterpret_cast<const uint4*>(p.w + (int64_t)n * p.K + kb + 16 * cc)
+                      : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, row = c >> 3, cc = c & 7;
+      *reinterpret_cast<uint4*>(&as[row * kF8P + 16 * cc]) = ra[i];
+      *reinterpret_cast<uint4*>(&ws[row * kF8P + 16 * cc]) = rw[i];
+    }
+  };
+  auto frag = [&](const uint8_t* base, int row) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * kF8P + 32 * g4);
+    const uint4 hi = *reinterpret_cast<const uint4*>(base + row * kF8P + 32 * g4 + 16);
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
+  stage();
+  __syncthreads();
+  for (int kb = 0; kb < p.K; kb += kF8K) {
+    const bool more = kb + kF8K < p.K;
+    if (more) fetch(kb + kF8K);
+    i32x8 af[4], wf[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      af[t] = frag(as, wm + 16 * t + i16);
+      wf[t] = frag(ws, wn + 16 * t + i16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], wf[j], acc[i][j], 0, 0,
+                                                                     0, 127, 0, 127);
+    __syncthreads();  // every wave done reading this step
+    if (more) {
+      stage();
+      __syncthreads();
+    }
+  }
+  TO* y = static_cast<TO*>(p.y);
+  float sa[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = m0 + wm + 16 * i + 4 * g4 + r;
+      sa[i][r] = m < p.rows ? p.sa[m] : 0.f;
+    }
+  if constexpr (sizeof(TO) == 2) {
+    // 16-bit output: the wave's 64 x 64 tile goes through LDS (rows of 144
+    // bytes; waves 0, 1 in the A buffer, 2, 3 in the W buffer; every read of
+    // both ended at the loop's last barrier) and leaves as 16-byte row chunks.
+    uint8_t* tile = (wave < 2 ? as : ws) + (wave & 1) * 64 * kF8P;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + 16 * j + i16;
+      const float sw = n < p.N ? p.sw[n] : 0.f;
+      const float b = (p.bias && n < p.N) ? ld_any(p.bias, p.bias_type, n) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<TO*>(&tile[(16 * i + 4 * g4 + r) * kF8P + 2 * (16 * j + i16)]) =
+              from_f32<TO>(acc[i][j][r] * sa[i][r] * sw + b);
+    }
+    asm volatile("" ::: "memory");  // the wave's tile writes before its reads
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = lane + 64 * q, row = c >> 3, cc = c & 7;
+      const int64_t m = m0 + wm + row;
+      const int n = n0 + wn + 8 * cc;
+      if (m >= p.rows || n >= p.N) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(&tile[row * kF8P + 16 * cc]);
+      if (n + 8 <= p.N && (reinterpret_cast<uintptr_t>(y + m * p.N + n) & 15) == 0) {
+        *reinterpret_cast<uint4*>(y + m * p.N + n) = v;
+      } else {
+        const TO* e = reinterpret_cast<const TO*>(&v);
+        for (int k = 0; k < 8 && n + k < p.N; ++k) y[m * p.N + n + k] = e[k];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + wn + 16 * j + i16;
+      if (n >= p.N) continue;
+      const float sw = p.sw[n];
+      const float b = p.bias ? ld_any(p.bias, p.bias_type, n) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t m = m0 + wm + 16 * i + 4 * g4 + r;
+          if (m >= p.rows) continue;
+          y[m * p.N + n] = from_f32<TO>(acc[i][j][r] * sa[i][r] * sw + b);
+        }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fp8_quant(const void* x, int io, int rows, int K, uint8_t* codes, float* scales,
@@ -133,6 +269,16 @@ hipError_t launch_fp8_quant(const void* x, int io, int rows, int K, uint8_t* cod
 hipError_t launch_fp8_linear(const Fp8Linear& p, int out_io, hipStream_t st) {
   if (p.rows <= 0) return hipSuccess;
   if (p.K % 32) return hipErrorInvalidValue;
+  if (p.K % kF8K == 0) {
+    const dim3 grid((p.N + kF8T - 1) / kF8T, (unsigned)((p.rows + kF8T - 1) / kF8T)), block(256);
+    if (out_io == kF32)
+      hipLaunchKernelGGL(fp8_linear_tiled_kernel<float>, grid, block, 0, st, p);
+    else if (out_io == kF16)
+      hipLaunchKernelGGL(fp8_linear_tiled_kernel<h16>, grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL(fp8_linear_tiled_kernel<b16>, grid, block, 0, st, p);
+    return hipGetLastError();
+  }
   const dim3 grid((p.N + 63) / 64, (unsigned)((p.rows + 63) / 64)), block(256);
   if (out_io == kF32)
     hipLaunchKernelGGL(fp8_linear_kernel<float>, grid, block, 0, st, p);
