@@ -22,7 +22,9 @@ Prints ONE JSON line on stdout (logs go to stderr) with:
   full_block   informational: the whole block forward (LayerNorms, attention,
                MLP, residual adds) of each workload's last block,
   backward     informational: the attention sub-layer backward of each
-               workload's last block (windows up to 16; float32 compute).
+               workload's last block (windows up to 16; float32 compute),
+  fp8_qkv      informational: the FP8 (E4M3) linear layer on each 16-bit
+               workload's QKV shape (quantisation and product timed apart).
 """
 from __future__ import annotations
 
@@ -44,6 +46,7 @@ METRIC = "shifted-window attention tokens/s + TFLOP/s as % of MFMA peak, 1 MI355
 MAIN = "swin_t_stage1_b64_fp16"
 PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0, "fp32": 157.3}   # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0                                             # HBM3E, MI355X
+PEAK_FP8_TFLOPS = 5000.0                                          # dense fp8 MFMA, MI355X
 ELEM = {"fp32": 4, "fp16": 2, "bf16": 2}
 
 
@@ -412,6 +415,44 @@ def backward_time(name, steps, warmup):
             "bwd_frac_of_fp32_mfma_peak": tf / PEAK_TFLOPS["fp32"], "compute": "fp32"}
 
 
+def fp8_time(name, steps, warmup):
+    """FP8 (E4M3) linear layer on the workload's QKV shape (tokens x 3C x C):
+    per-token quantisation of x and the scaled product, timed separately.
+    Informational; the product's roofline is the dense fp8 peak."""
+    import torch
+    import shifted_window_attention_roll_amd as swin
+    import workloads
+    case = workloads.make_workload(name)
+    if case.dtype == "fp32":
+        return None
+    blk = case.blocks[-1]
+    T, C = case.tokens, case.C
+    x = case.x.reshape(T, C).cuda()
+    qw, sw = swin.fp8_quantize(blk.w_qkv.cuda())
+    qa, sa = swin.fp8_quantize(x)
+    b = blk.b_qkv.cuda()
+    y = swin.fp8_linear(qa, sa, qw, sw, b, out_dtype=x.dtype)
+    for _ in range(warmup):
+        swin.fp8_quantize(x)
+        swin.fp8_linear(qa, sa, qw, sw, b, out=y)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(steps):
+        swin.fp8_quantize(x)
+    ev[1].record()
+    for _ in range(steps):
+        swin.fp8_linear(qa, sa, qw, sw, b, out=y)
+    ev[2].record()
+    torch.cuda.synchronize()
+    tq = ev[0].elapsed_time(ev[1]) / steps
+    tl = ev[1].elapsed_time(ev[2]) / steps
+    tf = 2.0 * T * 3 * C * C / (tl * 1e-3) / 1e12
+    del x, y, qa, sa
+    return {"shape": [T, 3 * C, C], "quantize_ms": tq, "linear_ms": tl, "linear_tflops": tf,
+            "frac_of_fp8_mfma_peak": tf / PEAK_FP8_TFLOPS}
+
+
 CALIB_BYTES = 256 << 20   # size of the plain device copy that calibrates the HBM counters
 CALIB_REPS = 4
 
@@ -562,12 +603,14 @@ def main():
                                                   ("tokens_per_s", "ms_per_step", "tflops",
                                                    "kernel_ms")}}))
     blocks = {}
-    backs = {}
+    backs, fp8s = {}, {}
     if not args.no_block:
         blocks[args.workload] = block_time(args.workload, min(args.steps, 20), 3)
         log(json.dumps({"workload": args.workload, **blocks[args.workload]}))
         backs[args.workload] = backward_time(args.workload, min(args.steps, 10), 2)
         log(json.dumps({"workload": args.workload, "backward": backs[args.workload]}))
+        fp8s[args.workload] = fp8_time(args.workload, min(args.steps, 10), 2)
+        log(json.dumps({"workload": args.workload, "fp8_qkv": fp8s[args.workload]}))
     others = {}
     if not args.no_others:
         for name in workloads.WORKLOADS:
@@ -583,6 +626,8 @@ def main():
                 log(json.dumps({"workload": name, **blocks[name]}))
                 backs[name] = backward_time(name, min(args.steps, 10), 2)
                 log(json.dumps({"workload": name, "backward": backs[name]}))
+                fp8s[name] = fp8_time(name, min(args.steps, 10), 2)
+                log(json.dumps({"workload": name, "fp8_qkv": fp8s[name]}))
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle")
@@ -616,6 +661,7 @@ def main():
         "workloads": others,
         "full_block": blocks,
         "backward": backs,
+        "fp8_qkv": fp8s,
         "source_digest": source_digest(),
     }
     del case
