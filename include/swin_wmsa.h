@@ -294,6 +294,34 @@ swin_status swin_fp8_linear(const unsigned char* a, const float* sa, const unsig
                             const float* sw, const void* bias, swin_dtype bias_dt, void* y,
                             swin_dtype y_dt, int rows, int N, int K, void* stream);
 
+/*
+ * 2:4 structured-sparse linear layers for the QKV and projection GEMMs.
+ *   Page: "Boost Vision Transformer with GPU-Friendly Sparsity and
+ *   Quantization", Section 3.1 / Figure 1 (two of every four consecutive
+ *   weights along the reduction dimension kept, stored as values plus
+ *   positions, run on sparse matrix cores) and Section 3.2 / Figure 3 (the
+ *   QKV, projection and feed-forward GEMMs).
+ *
+ * swin_sparse24_compress: w [N, K] (dt float16 or bfloat16) -> values [N, K/2]
+ * (dt; the two kept weights of each group of four along K, the lower position
+ * first) and codes [N, K/4] bytes (positions p0 | p1 << 2, p0 < p1).  Kept:
+ * the two largest magnitudes of the group (ties: the lower position).  K a
+ * multiple of 4, N >= 0 (SWIN_ERR_SHAPE); float32 is SWIN_ERR_DTYPE; outputs
+ * must not overlap w or each other (SWIN_ERR_ALIAS).
+ *
+ * swin_sparse24_linear: y [rows, N] = x [rows, K] wp^T + bias (dt, float32
+ * accumulation), wp the dense matrix the compressed form describes; bias [N]
+ * or NULL.  K a multiple of 64, N >= 1, rows >= 0 (SWIN_ERR_SHAPE); x and
+ * values 16-byte, codes 4-byte aligned (SWIN_ERR_ALIGN); y must not overlap
+ * an input (SWIN_ERR_ALIAS).
+ */
+swin_status swin_sparse24_compress(const void* w, swin_dtype dt, int N, int K, void* values,
+                                   unsigned char* codes, void* stream);
+
+swin_status swin_sparse24_linear(const void* x, const void* values, const unsigned char* codes,
+                                 const void* bias, void* y, swin_dtype dt, int rows, int N, int K,
+                                 void* stream);
+
 /* Workspace bytes of swin_wmsa_bwd (0 for an invalid descriptor or B == 0). */
 size_t swin_wmsa_bwd_workspace_size(const swin_wmsa_desc* desc);
 

@@ -24,7 +24,8 @@ _EXPORTS = ("swin_status_str", "swin_abi_version", "swin_partition_shift", "swin
             "swin_wmsa_kernel_count", "swin_wmsa_kernel_name", "swin_wmsa_fwd_timed",
             "swin_block_workspace_size", "swin_block_fwd", "swin_wmsa_bwd_workspace_size",
             "swin_wmsa_bwd", "swin_cpb_bwd_workspace_size", "swin_cpb_bwd",
-            "swin_fp8_quantize", "swin_fp8_linear")
+            "swin_fp8_quantize", "swin_fp8_linear", "swin_sparse24_compress",
+            "swin_sparse24_linear")
 
 
 class SwinDesc(ctypes.Structure):
@@ -103,6 +104,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swin_fp8_quantize.argtypes = [vp, i, i, i, vp, vp, vp]
     lib.swin_fp8_linear.restype = st
     lib.swin_fp8_linear.argtypes = [vp, vp, vp, vp, vp, i, vp, i, i, i, i, vp]
+    lib.swin_sparse24_compress.restype = st
+    lib.swin_sparse24_compress.argtypes = [vp, i, i, i, vp, vp, vp]
+    lib.swin_sparse24_linear.restype = st
+    lib.swin_sparse24_linear.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp]
     _lib = lib
     return lib
 
@@ -286,6 +291,29 @@ def fp8_linear(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: torch.Ten
         _ptr(a), _ptr(sa), _ptr(w), _ptr(sw), _ptr(bias),
         _DT[bias.dtype] if bias is not None else 0, _ptr(out), _DT[out.dtype], rows, N, K,
         _stream(stream)))
+    return out
+
+
+def sparse24_compress(w: torch.Tensor, stream=None):
+    """2:4 compressed form of a 16-bit weight [N, K]: (values [N, K/2], codes [N, K/4])."""
+    N, K = w.shape
+    vals = torch.empty(N, K // 2, dtype=w.dtype, device=w.device)
+    codes = torch.empty(N, K // 4, dtype=torch.uint8, device=w.device)
+    _check(load_library().swin_sparse24_compress(_ptr(w), _DT[w.dtype], N, K, _ptr(vals),
+                                                 _ptr(codes), _stream(stream)))
+    return vals, codes
+
+
+def sparse24_linear(x: torch.Tensor, vals: torch.Tensor, codes: torch.Tensor,
+                    bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    rows, K = x.shape
+    N = vals.shape[0]
+    if out is None:
+        out = torch.empty(rows, N, dtype=x.dtype, device=x.device)
+    _check(load_library().swin_sparse24_linear(_ptr(x), _ptr(vals), _ptr(codes), _ptr(bias),
+                                               _ptr(out), _DT[x.dtype], rows, N, K,
+                                               _stream(stream)))
     return out
 
 

@@ -481,3 +481,36 @@ swin_status swin_fp8_linear(const unsigned char* a, const float* sa, const unsig
   Fp8Linear p{a, sa, w, sw, bias, bias ? io_of(bias_dt) : kF32, y, rows, N, K};
   return from_hip(launch_fp8_linear(p, io_of(y_dt), static_cast<hipStream_t>(stream)));
 }
+
+// ---------------------------------------------------------------------------
+// 2:4 sparse linear layers.
+
+swin_status swin_sparse24_compress(const void* w, swin_dtype dt, int N, int K, void* values,
+                                   unsigned char* codes, void* stream) {
+  if (dt != SWIN_F16 && dt != SWIN_BF16) return SWIN_ERR_DTYPE;
+  if (N < 0 || K < 4 || K % 4) return SWIN_ERR_SHAPE;
+  if (N == 0) return SWIN_OK;
+  if (!w || !values || !codes) return SWIN_ERR_NULL;
+  const size_t wb = (size_t)N * K * 2, vb = wb / 2, cb = (size_t)N * K / 4;
+  if (overlap(values, vb, w, wb) || overlap(codes, cb, w, wb) || overlap(values, vb, codes, cb))
+    return SWIN_ERR_ALIAS;
+  return from_hip(launch_prune24(w, io_of(dt), N, K, values, codes,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+swin_status swin_sparse24_linear(const void* x, const void* values, const unsigned char* codes,
+                                 const void* bias, void* y, swin_dtype dt, int rows, int N, int K,
+                                 void* stream) {
+  if (dt != SWIN_F16 && dt != SWIN_BF16) return SWIN_ERR_DTYPE;
+  if (rows < 0 || N < 1 || K < 64 || K % 64) return SWIN_ERR_SHAPE;
+  if (rows == 0) return SWIN_OK;
+  if (!x || !values || !codes || !y) return SWIN_ERR_NULL;
+  const size_t yb = (size_t)rows * N * 2;
+  if (overlap(y, yb, x, (size_t)rows * K * 2) || overlap(y, yb, values, (size_t)N * K) ||
+      overlap(y, yb, codes, (size_t)N * K / 4) || (bias && overlap(y, yb, bias, (size_t)N * 2)))
+    return SWIN_ERR_ALIAS;
+  if (!aligned16(x) || !aligned16(values) || (reinterpret_cast<uintptr_t>(codes) & 3))
+    return SWIN_ERR_ALIGN;
+  Sparse24Linear p{x, values, codes, bias, y, rows, N, K};
+  return from_hip(launch_sparse24_linear(p, io_of(dt), static_cast<hipStream_t>(stream)));
+}

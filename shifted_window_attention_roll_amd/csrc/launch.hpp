@@ -153,6 +153,20 @@ hipError_t launch_fp8_quant(const void* x, int io, int rows, int K, uint8_t* cod
                             hipStream_t st);
 hipError_t launch_fp8_linear(const Fp8Linear& p, int out_io, hipStream_t st);
 
+// 2:4 sparse linear layers (sparse.hip).
+struct Sparse24Linear {
+  const void* x;         // [rows, K]
+  const void* vals;      // [N, K/2]
+  const uint8_t* codes;  // [N, K/4]
+  const void* bias;      // [N] or null
+  void* y;               // [rows, N]
+  int64_t rows;
+  int N, K;
+};
+hipError_t launch_prune24(const void* w, int io, int N, int K, void* vals, uint8_t* codes,
+                          hipStream_t st);
+hipError_t launch_sparse24_linear(const Sparse24Linear& p, int io, hipStream_t st);
+
 inline int max_window(int io_bytes) { return io_bytes == 4 ? 16 : 24; }
 
 }  // namespace swin

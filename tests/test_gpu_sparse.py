@@ -1,0 +1,82 @@
+"""GPU parity of the 2:4 sparse linear layers (swin_sparse24_compress,
+swin_sparse24_linear through the C ABI) against oracle/swin_sparse.py.
+
+The compressed form is a selection (values copied, positions integers):
+compared bit for bit.  The product: float32 accumulation of 16-bit products
+(exact in float32), y rounded once, so per element |gpu - oracle| <= u |oracle|
++ 2 K 2^-24 (|x| |wp|^T) (u = 2^-11 float16, 2^-8 bfloat16), derived."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import swin_sparse as sp
+
+pytestmark = pytest.mark.gpu
+U = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import shifted_window_attention_roll_amd as swin
+    swin.load_library()
+    return swin
+
+
+@pytest.mark.parametrize("N,K,dtype", [(96, 96, "bf16"), (288, 512, "fp16"), (7, 4, "bf16")])
+def test_compress_bit_exact(gpu, N, K, dtype):
+    _say(f"sparse24 compress N={N} K={K} {dtype}")
+    w = workloads.make_upstream_grad((N, K), dtype, N + K, std=0.02)
+    w[0, :4] = torch.tensor([1.0, -1.0, 1.0, 1.0])     # ties: the lower positions
+    vals, codes = gpu.sparse24_compress(w.cuda())
+    torch.cuda.synchronize()
+    wp = sp.prune24(workloads.f64(w))
+    ov, oc = sp.compress24(wp)
+    np.testing.assert_array_equal(codes.cpu().numpy(), oc)
+    np.testing.assert_array_equal(workloads.f64(vals.cpu()), ov)
+
+
+@pytest.mark.parametrize("rows,N,K,dtype", [(100, 96, 64, "bf16"), (64, 288, 128, "fp16"),
+                                            (37, 1536, 512, "bf16"), (256, 512, 2048, "fp16")])
+def test_linear(gpu, rows, N, K, dtype):
+    _say(f"sparse24 linear rows={rows} N={N} K={K} {dtype}")
+    x = workloads.make_upstream_grad((rows, K), dtype, rows + 3 * K)
+    w = workloads.make_upstream_grad((N, K), dtype, N + 5 * K, std=0.02)
+    b = workloads.make_upstream_grad((N,), dtype, N + 9, std=0.1)
+    vals, codes = gpu.sparse24_compress(w.cuda())
+    y = gpu.sparse24_linear(x.cuda(), vals, codes, b.cuda())
+    torch.cuda.synchronize()
+    wp = sp.prune24(workloads.f64(w))
+    ref = sp.linear_sparse24(workloads.f64(x), wp, workloads.f64(b))
+    bound = U[dtype] * np.abs(ref) + 2 * K * 2.0 ** -24 * (np.abs(workloads.f64(x)) @ np.abs(wp).T)
+    err = np.abs(workloads.f64(y.cpu()) - ref)
+    _say(f"  max err {err.max():.3g}, max err / bound {float((err / bound).max()):.3g}")
+    assert np.all(err <= bound)
+
+
+def test_linear_workload_qkv_sampled(gpu):
+    case = workloads.make_workload("swinv2_g_stage1_384_w24_bf16")
+    blk = case.blocks[-1]
+    T, C = case.tokens, case.C
+    _say(f"sparse24 linear SwinV2-G stage 1 QKV: {T} x {3 * C} x {C}")
+    x = case.x.reshape(T, C)
+    vals, codes = gpu.sparse24_compress(blk.w_qkv.cuda())
+    y = gpu.sparse24_linear(x.cuda(), vals, codes, blk.b_qkv.cuda())
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(2).choice(T, 64, replace=False)
+    wp = sp.prune24(workloads.f64(blk.w_qkv))
+    xs = workloads.f64(x[rows])
+    ref = sp.linear_sparse24(xs, wp, workloads.f64(blk.b_qkv))
+    bound = U["bf16"] * np.abs(ref) + 2 * C * 2.0 ** -24 * (np.abs(xs) @ np.abs(wp).T)
+    err = np.abs(workloads.f64(y[rows].cpu()) - ref)
+    _say(f"  max err {err.max():.3g}, max err / bound {float((err / bound).max()):.3g}")
+    assert np.all(err <= bound)
