@@ -24,7 +24,8 @@ Prints ONE JSON line on stdout (logs go to stderr) with:
   backward     informational: the attention sub-layer backward of each
                workload's last block (windows up to 16; float32 compute),
   fp8_qkv      informational: the FP8 (E4M3) linear layer on each 16-bit
-               workload's QKV shape (quantisation and product timed apart).
+               workload's QKV shape (quantisation and product timed apart),
+               and the 2:4-sparse linear layer on the same shape.
 """
 from __future__ import annotations
 
@@ -448,9 +449,25 @@ def fp8_time(name, steps, warmup):
     tq = ev[0].elapsed_time(ev[1]) / steps
     tl = ev[1].elapsed_time(ev[2]) / steps
     tf = 2.0 * T * 3 * C * C / (tl * 1e-3) / 1e12
+    out = {"shape": [T, 3 * C, C], "quantize_ms": tq, "linear_ms": tl, "linear_tflops": tf,
+           "frac_of_fp8_mfma_peak": tf / PEAK_FP8_TFLOPS}
+    if C % 64 == 0:
+        # The same shape with 2:4-pruned weights on the sparse matrix cores
+        # (flops counted as the dense product's; peak: dense 16-bit x 2).
+        vals, codes = swin.sparse24_compress(blk.w_qkv.cuda())
+        for _ in range(warmup):
+            swin.sparse24_linear(x, vals, codes, b, out=y)
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(steps):
+            swin.sparse24_linear(x, vals, codes, b, out=y)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ts = ev[0].elapsed_time(ev[1]) / steps
+        out["sparse24_linear_ms"] = ts
+        out["sparse24_dense_equiv_tflops"] = 2.0 * T * 3 * C * C / (ts * 1e-3) / 1e12
     del x, y, qa, sa
-    return {"shape": [T, 3 * C, C], "quantize_ms": tq, "linear_ms": tl, "linear_tflops": tf,
-            "frac_of_fp8_mfma_peak": tf / PEAK_FP8_TFLOPS}
+    return out
 
 
 CALIB_BYTES = 256 << 20   # size of the plain device copy that calibrates the HBM counters

@@ -120,11 +120,16 @@ __global__ __launch_bounds__(256) void sparse24_linear_kernel(Sparse24Linear p) 
     for (int j = 0; j < 2; ++j) {
       const int64_t t = tr[j];
       if (t >= p.rows) continue;
+      const int nb = n0 + 16 * i + 4 * g4;
+      T v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n0 + 16 * i + 4 * g4 + r;
-        if (n >= p.N) continue;
-        y[t * p.N + n] = from_f32<T>(acc[i][j][r] + (bias ? (float)bias[n] : 0.f));
+      for (int r = 0; r < 4; ++r)
+        v[r] = from_f32<T>(acc[i][j][r] + ((bias && nb + r < p.N) ? (float)bias[nb + r] : 0.f));
+      T* dst = y + t * p.N + nb;
+      if (nb + 4 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 7) == 0) {
+        *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, v);  // 4 channels at once
+      } else {
+        for (int r = 0; r < 4 && nb + r < p.N; ++r) dst[r] = v[r];
       }
     }
 }
