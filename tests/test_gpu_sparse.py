@@ -46,6 +46,7 @@ def test_compress_bit_exact(gpu, N, K, dtype):
 
 
 @pytest.mark.parametrize("rows,N,K,dtype", [(100, 96, 64, "bf16"), (64, 288, 128, "fp16"),
+                                            (50, 90, 128, "fp16"),   # N % 4 != 0: untiled kernel
                                             (37, 1536, 512, "bf16"), (256, 512, 2048, "fp16")])
 def test_linear(gpu, rows, N, K, dtype):
     _say(f"sparse24 linear rows={rows} N={N} K={K} {dtype}")
