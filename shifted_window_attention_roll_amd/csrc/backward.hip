@@ -13,7 +13,7 @@
 //   per (window, head): recompute S, P and O; dq, dk, dv; table and tau
 //   gradients                                                     (attn_bwd)
 //   dWp = dyw^T o, dWqkv = dqkv^T xw (split over tokens, atomics) (bwd_gemm)
-//   dbp, dbqkv = column sums of dyw, dqkv                         (colsum)
+//   dbp, dbqkv = column sums of dyw, dqkv (in the same two GEMMs)
 //   dxw = dqkv Wqkv, dx = reverse+unshift(dxw)                    (bwd_gemm,
 //                                                                   index map)
 // The inverse of a permutation is its adjoint, so the index maps of the
@@ -80,6 +80,10 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm a) {
   f32x4 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Row sums of A (the bias gradient of a weight-gradient product), from the
+  // staged runs of the first column tile's workgroups.
+  const bool rows_sum = ATOMIC && a.rowsum && !a_k_unit && blockIdx.x == 0;
+  float rs[8] = {};
   for (int64_t kb = k0; kb < k1; kb += kGK) {
     // Each thread stages one run of 8 elements of each operand along its
     // unit-stride dimension (k, or the row dimension m / n).
@@ -96,6 +100,10 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm a) {
         load_run8(A, m + k * a.sak, k < k1 ? (int)min<int64_t>(a.M - m, 8) : 0, v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) As[(mm + i) * kGP + kk] = v[i];
+        if (rows_sum) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) rs[i] += v[i];
+        }
       }
       if (!b_n_unit) {
         const int nn = tid >> 2, kk = (tid & 3) * 8;
@@ -131,6 +139,19 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm a) {
       for (int j = 0; j < 2; ++j) acc[i][j] = mma_16x16x32(af[i], bf[j], acc[i][j]);
     __syncthreads();
   }
+  if (rows_sum) {
+    // Thread t staged rows 8 (t % 8) .. +7 at k = t / 8 of every step: sum the
+    // 32 threads of each row group through LDS (the last barrier ended every
+    // read of As).
+#pragma unroll
+    for (int i = 0; i < 8; ++i) As[(tid >> 3) * 64 + (tid & 7) * 8 + i] = rs[i];
+    __syncthreads();
+    if (tid < 64 && m0 + tid < a.M) {
+      float s = 0.f;
+      for (int q = 0; q < 32; ++q) s += As[q * 64 + tid];
+      atomicAdd(a.rowsum + m0 + tid, s);
+    }
+  }
   // Lane l holds column l % 16 of rows 4 (l / 16) .. +3 of each 16 x 16 tile.
   TC* C = static_cast<TC*>(a.C);
   const bool add_bias = a.bias && (!ATOMIC || blockIdx.z == 0);
@@ -152,19 +173,6 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm a) {
           C[m * a.ldc + n] = from_f32<TC>(v);
       }
   }
-}
-
-// out[c] += sum over rows [z*rc, (z+1)*rc) of src[r*ld + c]; one column per thread.
-template <typename T>
-__global__ __launch_bounds__(256) void colsum_kernel(const T* src, int64_t rows, int cols,
-                                                     int64_t ld, int64_t rc, float* out) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
-  const int64_t r0 = (int64_t)blockIdx.y * rc;
-  const int64_t r1 = r0 + rc < rows ? r0 + rc : rows;
-  float s = 0.f;
-  for (int64_t r = r0; r < r1; ++r) s += (float)src[r * ld + c];
-  atomicAdd(out + c, s);
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
@@ -572,21 +580,6 @@ hipError_t gemm_launch(const BwdGemm& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t colsum_launch(const T* src, int64_t rows, int cols, int64_t ld, float* out,
-                         hipStream_t st) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  const int cb = (cols + 255) / 256;
-  int64_t splits = 2048 / cb;
-  if (splits > rows) splits = rows;
-  if (splits < 1) splits = 1;
-  const int64_t rc = (rows + splits - 1) / splits;
-  splits = (rows + rc - 1) / rc;
-  hipLaunchKernelGGL((colsum_kernel<T>), dim3(cb, (unsigned)splits), dim3(256), 0, st, src, rows,
-                     cols, ld, rc, out);
-  return hipGetLastError();
-}
-
 hipError_t zero(float* p, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
@@ -639,27 +632,27 @@ hipError_t backward(const BwdArgs& a, hipStream_t st) {
   p.qkv = a.qkv; p.dout = a.dout; p.table = a.table; p.tau = a.tau;
   p.o = a.o; p.dqkv = a.dqkv; p.dtable = a.dtable; p.dtau = a.dtau;
   const int items = g.B * g.nW * g.heads;
-if (g.N <= 32) attn_bwd_launch<32>(p, a.v2, items, st);
+  if (g.N <= 32) attn_bwd_launch<32>(p, a.v2, items, st);
   else if (g.N <= 64) attn_bwd_launch<64>(p, a.v2, items, st);
   else if (g.N <= 128) attn_bwd_launch<128>(p, a.v2, items, st);
   else attn_bwd_launch<256>(p, a.v2, items, st);
   TRY(hipGetLastError());
-  // dWp = dyw^T o   [C, C];  dbp = colsum(dyw)
+  // dWp = dyw^T o   [C, C];  dbp = column sums of dyw
   BwdGemm wp{};
   wp.M = C; wp.N = C; wp.K = T_;
   wp.A = a.dyw; wp.sam = 1; wp.sak = C;
   wp.B = a.o; wp.sbk = C; wp.sbn = 1;
   wp.C = a.dw_proj; wp.ldc = C;
+  wp.rowsum = a.db_proj;  // dbp = column sums of dyw
   TRY((gemm_launch<T, float, float, true>(wp, st)));
-  TRY(colsum_launch<T>(static_cast<const T*>(a.dyw), T_, C, C, a.db_proj, st));
-  // dWqkv = dqkv^T xw   [3C, C];  dbqkv = colsum(dqkv)
+  // dWqkv = dqkv^T xw   [3C, C];  dbqkv = column sums of dqkv
   BwdGemm wq{};
   wq.M = 3 * C; wq.N = C; wq.K = T_;
   wq.A = a.dqkv; wq.sam = 1; wq.sak = 3 * C;
   wq.B = a.xw; wq.sbk = C; wq.sbn = 1;
   wq.C = a.dw_qkv; wq.ldc = C;
+  wq.rowsum = a.db_qkv;  // dbqkv = column sums of dqkv
   TRY((gemm_launch<float, T, float, true>(wq, st)));
-  TRY(colsum_launch<float>(a.dqkv, T_, 3 * C, 3 * C, a.db_qkv, st));
   // dxw = dqkv Wqkv   [T, C], then back to image order.
   BwdGemm dx{};
   dx.M = T_; dx.N = C; dx.K = 3 * C;

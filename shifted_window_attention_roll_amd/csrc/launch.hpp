@@ -104,6 +104,7 @@ struct BwdGemm {
   const void* bias;  // [N], B's element type, or null
   void* C;
   int64_t ldc;
+  float* rowsum;     // ATOMIC with sam == 1 only: += sum_k A(m, k), or null
 };
 struct AttnBwd {
   Geom g;
