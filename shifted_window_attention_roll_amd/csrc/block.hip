@@ -233,7 +233,13 @@ struct MlpArgs {
 template <typename T, int C, bool V1>
 __global__ __launch_bounds__(256) void mlp_fused_kernel(MlpArgs<T> p) {
   constexpr int KC = C / 32, CT = C / 16, RT = kMlpRT;
+  // C = 128: the chunk's weights are staged in LDS for the 4 waves (measured
+  // faster at SwinV2-B stage 1); smaller C keeps them in registers from L2
+  // (more waves fit; measured faster at Swin-T stage 1).
+  constexpr bool STAGE_W = C >= 128;
   __shared__ __attribute__((aligned(16))) T hs[4][RT][16 * kMlpLD];
+  __shared__ __attribute__((aligned(16))) T w1s[STAGE_W ? 32 * (C + 8) : 8];
+  __shared__ __attribute__((aligned(16))) T w2s[STAGE_W ? C * 40 : 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g4 = lane >> 4;
   const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * 16 * RT;
@@ -291,6 +297,83 @@ __global__ __launch_bounds__(256) void mlp_fused_kernel(MlpArgs<T> p) {
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) yacc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (STAGE_W) {
+  // The weights of a 32-unit hidden chunk (W1 rows hc .. +31, W2 columns hc ..
+  // +31) go through LDS, shared by the 4 waves; the next chunk's 16-byte
+  // pieces are loaded into registers during this chunk's products.
+  constexpr int P1 = C + 8, P2 = 40;          // LDS row pitches (elements)
+  constexpr int PER = (8 * C) / 256;          // 16-byte pieces per thread
+  static_assert(PER * 256 == 8 * C, "chunk split");
+  uint4 pre[PER];
+  auto fetch_w = [&](int hc) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      if (e < 4 * C) {  // W1: 32 rows x C/8 pieces
+        const int row = e / (C / 8), c8 = e - row * (C / 8);
+        pre[i] = gload16(p.w1 + (int64_t)(hc + row) * C + 8 * c8);
+      } else {          // W2: C rows x 4 pieces
+        const int f = e - 4 * C, row = f >> 2, c8 = f & 3;
+        pre[i] = gload16(p.w2 + (int64_t)row * hidden + hc + 8 * c8);
+      }
+    }
+  };
+  auto store_w = [&]() {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      if (e < 4 * C) {
+        const int row = e / (C / 8), c8 = e - row * (C / 8);
+        *reinterpret_cast<uint4*>(&w1s[row * P1 + 8 * c8]) = pre[i];
+      } else {
+        const int f = e - 4 * C, row = f >> 2, c8 = f & 3;
+        *reinterpret_cast<uint4*>(&w2s[row * P2 + 8 * c8]) = pre[i];
+      }
+    }
+  };
+  fetch_w(0);
+  store_w();
+  __syncthreads();
+  for (int hc = 0; hc < hidden; hc += 32) {
+    const bool more = hc + 32 < hidden;
+    if (more) fetch_w(hc + 32);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int n = hc + 16 * t + i16;  // this lane's hidden unit (B column)
+      vec8<T> wb[KC];
+#pragma unroll
+      for (int kk = 0; kk < KC; ++kk) wb[kk] = load8(&w1s[(16 * t + i16) * P1 + 32 * kk + 8 * g4]);
+      const float bn = p.b1 ? (float)p.b1[n] : 0.f;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4 h = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) h = mma_16x16x32(xa[rt][kk], wb[kk], h);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v = h[q] + bn;
+          hs[wave][rt][(4 * g4 + q) * kMlpLD + 16 * t + i16] =
+              from_f32<T>(0.5f * v * (1.0f + erff(v * 0.70710678118654752f)));
+        }
+      }
+    }
+    asm volatile("" ::: "memory");  // the wave's tile writes before its reads
+    vec8<T> wb2[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) wb2[ct] = load8(&w2s[(16 * ct + i16) * P2 + 8 * g4]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const vec8<T> ha = load8(&hs[wave][rt][i16 * kMlpLD + 8 * g4]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) yacc[rt][ct] = mma_16x16x32(ha, wb2[ct], yacc[rt][ct]);
+    }
+    __syncthreads();  // every wave done with this chunk's weights (and its tile)
+    if (more) {
+      store_w();
+      __syncthreads();
+    }
+  }
+  } else {
   for (int hc = 0; hc < hidden; hc += 32) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -324,6 +407,7 @@ __global__ __launch_bounds__(256) void mlp_fused_kernel(MlpArgs<T> p) {
       for (int ct = 0; ct < CT; ++ct) yacc[rt][ct] = mma_16x16x32(ha, wb2[ct], yacc[rt][ct]);
     }
     asm volatile("" ::: "memory");  // reads done before the next chunk's writes
+  }
   }
   // Lane: channel 16 ct + i16 of rows 4 g4 + q of each row tile.
   float bc[CT], gc[CT], bec[CT];
