@@ -56,14 +56,15 @@ def _assert_block_close(y, ref, dtype, what):
     assert rel <= 1e-2, f"{what}: rel-L2 {rel:.3e}"
 
 
-def _setup(B, H, W, C, heads, M, s, dtype, mode, seed):
+def _setup(B, H, W, C, heads, M, s, dtype, mode, seed, hidden=None):
     # MLP weights: N(0, 0.02) in 16 bits (the recipe of the attention weights;
     # the MLP branch is then 5-10 % of the residual stream), N(0, 0.1) in float32
     # (an O(1) branch, checked at the float32 bar).
     case = workloads.make_case(B, H, W, C, heads, M, (s,), dtype, mode, seed=seed, w_std=0.08,
                                bias_std=0.05, tau="uniform")
     blk = case.blocks[0]
-    extra = workloads.make_block_params(C, dtype, seed + 1, fc_std=0.1 if dtype == "fp32" else 0.02)
+    extra = workloads.make_block_params(C, dtype, seed + 1, hidden=hidden,
+                                        fc_std=0.1 if dtype == "fp32" else 0.02)
     dev = "cuda"
     gp = {"w_qkv": blk.w_qkv.to(dev), "b_qkv": blk.b_qkv.to(dev), "w_proj": blk.w_proj.to(dev),
           "b_proj": blk.b_proj.to(dev), "table": helpers.gpu_table(case, blk, dev)}
@@ -123,3 +124,21 @@ def test_block_deterministic_and_written(gpu):
     torch.cuda.synchronize()
     assert torch.isfinite(y1.float()).all()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("C,heads,dtype,mode,hidden", [
+    (64, 2, "bf16", "v1", 32),     # one hidden chunk
+    (64, 2, "fp16", "v2", 160),    # hidden not 4C
+    (128, 4, "bf16", "v1", 96),    # LDS-staged weights, three chunks
+    (96, 3, "fp16", "v1", 544),    # 17 chunks
+])
+def test_block_fused_mlp_hidden_widths(gpu, C, heads, dtype, mode, hidden):
+    _say(f"block fused MLP C={C} hidden={hidden} {dtype} {mode}")
+    M = 8 if C != 96 else 7
+    H = W = 2 * M
+    case, blk, gp, op = _setup(2, H, W, C, heads, M, M // 2, dtype, mode, seed=C + hidden,
+                               hidden=hidden)
+    y = gpu.block_fwd(case.x.cuda(), gp, M, M // 2, heads, mode)
+    torch.cuda.synchronize()
+    ref = sb.block_forward(workloads.f64(case.x), op, M, M // 2, heads, mode)
+    _assert_block_close(workloads.f64(y.cpu()), ref, dtype, "block hidden")
