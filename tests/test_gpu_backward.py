@@ -171,3 +171,21 @@ def test_cpb_backward(gpu, M, hidden, heads):
         err = float(np.abs(g - r).max())
         _say(f"  {k}: max err {err:.3g} (scale {scale:.3g})")
         assert err <= TOL * scale, (k, err, scale)
+
+
+def test_backward_large_bias(gpu):
+    # A bias table with std 4 (logit spreads of tens): the exact row maxima keep
+    # every exponential finite; gradients still at the bar.
+    _say("bwd large bias")
+    case = workloads.make_case(1, 16, 16, 64, 2, 8, (4,), "fp32", "v1", seed=31, w_std=0.08,
+                               bias_std=0.1, table_std=4.0)
+    blk = case.blocks[0]
+    dy = workloads.make_upstream_grad(case.x.shape, "fp32", 32)
+    g = gpu.wmsa_bwd(case.x.cuda(), blk.w_qkv.cuda(), blk.b_qkv.cuda(), blk.w_proj.cuda(),
+                     blk.table.cuda(), dy.cuda(), 8, 4, 2, "v1")
+    torch.cuda.synchronize()
+    ref = sbw.wmsa_backward(workloads.f64(case.x), workloads.f64(blk.w_qkv),
+                            workloads.f64(blk.b_qkv), workloads.f64(blk.w_proj),
+                            workloads.f64(blk.b_proj), workloads.f64(blk.table), 8, 4, 2,
+                            workloads.f64(dy), "v1")
+    _assert_grads(g, ref, "fp32", "v1", "large bias")

@@ -111,3 +111,16 @@ def test_linear_workload_qkv_sampled(gpu, name):
     qwo, swo = f8.quantize_rows(blk.w_qkv.float().numpy())
     _check_linear(workloads.f64(y[rows].cpu()), qao, sao, qwo, swo, workloads.f64(blk.b_qkv),
                   x.dtype)
+
+
+def test_linear_without_bias(gpu):
+    _say("fp8 linear without bias")
+    x = workloads.make_upstream_grad((40, 256), "bf16", 5)
+    w = workloads.make_upstream_grad((128, 256), "bf16", 6, std=0.02)
+    qa, sa = gpu.fp8_quantize(x.cuda())
+    qw, sw = gpu.fp8_quantize(w.cuda())
+    y = gpu.fp8_linear(qa, sa, qw, sw, None, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    qao, sao = f8.quantize_rows(x.float().numpy())
+    qwo, swo = f8.quantize_rows(w.float().numpy())
+    _check_linear(workloads.f64(y.cpu()), qao, sao, qwo, swo, None, torch.bfloat16)

@@ -81,3 +81,16 @@ def test_linear_workload_qkv_sampled(gpu):
     err = np.abs(workloads.f64(y[rows].cpu()) - ref)
     _say(f"  max err {err.max():.3g}, max err / bound {float((err / bound).max()):.3g}")
     assert np.all(err <= bound)
+
+
+def test_linear_without_bias(gpu):
+    _say("sparse24 linear without bias")
+    x = workloads.make_upstream_grad((70, 128), "fp16", 8)
+    w = workloads.make_upstream_grad((64, 128), "fp16", 9, std=0.02)
+    vals, codes = gpu.sparse24_compress(w.cuda())
+    y = gpu.sparse24_linear(x.cuda(), vals, codes, None)
+    torch.cuda.synchronize()
+    wp = sp.prune24(workloads.f64(w))
+    ref = sp.linear_sparse24(workloads.f64(x), wp)
+    bound = U["fp16"] * np.abs(ref) + 2 * 128 * 2.0 ** -24 * (np.abs(workloads.f64(x)) @ np.abs(wp).T)
+    assert np.all(np.abs(workloads.f64(y.cpu()) - ref) <= bound)
