@@ -4,8 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
 A step is one pass of the whole forward over one batch: for the default
-workload (Swin-T stage 1, batch 64, 56x56 tokens, C = 96, 3 heads, window 7,
-fp16) that is a W-MSA block (shift 0) followed by an SW-MSA block (shift 3).
+workload (SwinV2-G-like stage 1: one 1536 x 1536 image at patch 4, i.e. 384 x
+384 tokens, C = 512, 16 heads, window 24, shift 12, scaled cosine attention,
+bf16) that is one SW-MSA block forward.
 Inputs are seeded synthetic tensors already resident in HBM; x is rotated over
 enough copies to exceed the 256 MB last-level cache.
 
@@ -44,7 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "shifted-window attention tokens/s + TFLOP/s as % of MFMA peak, 1 MI355X"
-MAIN = "swin_t_stage1_b64_fp16"
+MAIN = "swinv2_g_stage1_384_w24_bf16"
 PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0, "fp32": 157.3}   # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0                                             # HBM3E, MI355X
 PEAK_FP8_TFLOPS = 5000.0                                          # dense fp8 MFMA, MI355X
@@ -267,42 +268,74 @@ def roofline(runner, kern_ms):
     return r
 
 
+def _sample_windows(B, H, W, M, n):
+    """n windows spread evenly over the batch (every stride-th window, so the
+    masked last row / column of the grid is represented)."""
+    total = B * (H // M) * (W // M)
+    n = max(1, min(n, total))
+    return sorted({int(round(i * (total - 1) / max(n - 1, 1))) for i in range(n)})
+
+
 def cpu_baseline(name, budget_s=15.0):
-    """The float64 oracle as it stands, on the first images of the workload."""
-    import numpy as np
+    """The float64 oracle as it stands, on a bounded sample of the workload: whole
+    images when the batch has several, else a subset of the image's windows."""
     import workloads
     from oracle import swin_oracle as so
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity set
-        threads = len(os.sched_getaffinity(0))
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: BLAS thread count unknown
+        blas = None
     case = workloads.make_workload(name)
+    N = case.M * case.M
+    tables = []
+    for blk in case.blocks:
+        tables.append(workloads.f64(blk.table) if case.mode == "v1" else
+                      so.cpb_table(workloads.f64(blk.cpb_w1), workloads.f64(blk.cpb_b1),
+                                   workloads.f64(blk.cpb_w2), workloads.f64(blk.cpb_b2), case.M))
 
-    def run(nimg):
-        x = workloads.f64(case.x[:nimg])
-        t0 = time.perf_counter()
-        for blk in case.blocks:
-            table = (workloads.f64(blk.table) if case.mode == "v1" else
-                     so.cpb_table(workloads.f64(blk.cpb_w1), workloads.f64(blk.cpb_b1),
-                                  workloads.f64(blk.cpb_w2), workloads.f64(blk.cpb_b2), case.M))
-            x = so.wmsa_forward(x, workloads.f64(blk.w_qkv), workloads.f64(blk.b_qkv),
-                                workloads.f64(blk.w_proj), workloads.f64(blk.b_proj), table,
-                                case.M, blk.s, case.heads, case.mode,
-                                tau=None if blk.tau is None else workloads.f64(blk.tau))
-        return time.perf_counter() - t0
+    def fwd(blk, table, x, windows=None):
+        return so.wmsa_forward(x, workloads.f64(blk.w_qkv), workloads.f64(blk.b_qkv),
+                               workloads.f64(blk.w_proj), workloads.f64(blk.b_proj), table,
+                               case.M, blk.s, case.heads, case.mode,
+                               tau=None if blk.tau is None else workloads.f64(blk.tau),
+                               windows=windows)
 
-    t1 = run(1)
-    nimg = int(max(1, min(case.B, budget_s / max(t1, 1e-3))))
-    t, passes = 0.0, 0
+    if case.B > 1:
+        def run(n):
+            x = workloads.f64(case.x[:n])
+            t0 = time.perf_counter()
+            for blk, table in zip(case.blocks, tables):
+                x = fwd(blk, table, x)
+            return time.perf_counter() - t0, n * case.H * case.W * len(case.blocks)
+        unit, limit = "image", case.B
+    else:
+        x64 = workloads.f64(case.x)
+        nwin = (case.H // case.M) * (case.W // case.M)
+
+        def run(n):
+            wins = _sample_windows(1, case.H, case.W, case.M, n)
+            t0 = time.perf_counter()
+            for blk, table in zip(case.blocks, tables):
+                fwd(blk, table, x64, windows=wins)
+            return time.perf_counter() - t0, len(wins) * N * len(case.blocks)
+        unit, limit = "window", nwin
+
+    t1, _ = run(1)
+    n = int(max(1, min(limit, budget_s / max(t1, 1e-3) / 2)))
+    t, tokens, passes = 0.0, 0, 0
     while passes == 0 or (t < 0.66 * budget_s and passes < 100):
-        t += run(nimg)
+        dt, tok = run(n)
+        t += dt
+        tokens += tok
         passes += 1
-    tokens = passes * nimg * case.H * case.W * len(case.blocks)
-    return {"value": tokens / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} pass(es) over {nimg} of {case.B} images of {name}, all "
+    return {"value": tokens / t, "unit": "tokens/s", "cores": blas or affinity, "kind": "oracle",
+            "affinity_cores": affinity, "blas_threads": blas,
+            "sample": f"{passes} pass(es) over {n} of {limit} {unit}s of {name}, all "
                       f"{len(case.blocks)} block(s), {tokens} block-tokens in {t:.2f} s "
-                      f"(float64 numpy, BLAS threads={threads})"}
+                      f"(float64 numpy; {affinity} cores in the affinity set, BLAS threads "
+                      f"{blas})"}
 
 
 def measure(name, steps, warmup, hip):
@@ -570,6 +603,108 @@ def traffic_summarize(name, fetch_dir, write_dir, command):
     print("\n".join(lines))
 
 
+def _stats_rows(d):
+    import csv
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    return rows
+
+
+def trace_summarize(name, trace_dir, command):
+    """rocprofv3 --kernel-trace --stats output -> profiles/kernel_trace_<workload>.md:
+    per kernel of the forward, calls, average / min / max duration and the
+    algorithmic rate that average gives."""
+    import workloads
+    import shifted_window_attention_roll_amd as swin
+    case = workloads.make_workload(name)
+    desc = swin.make_desc(case.B, case.H, case.W, case.C, case.heads, case.M,
+                          case.blocks[0].s, case.mode, case.torch_dtype)
+    kernels = swin.kernel_names(desc)
+    work = stage_work(case)
+    peak_f = PEAK_TFLOPS[case.dtype]
+    lines = [f"# Kernel trace, {name}", "", f"Command: `{command}`", "",
+             "Durations from rocprofv3 `--kernel-trace --stats` (every launch of the run, "
+             "warm-up included).  Rate = the kernel's algorithmic flops (bytes) per launch / "
+             "its average duration.", "",
+             "| kernel | calls | avg us | min us | max us | algorithmic GFLOP | TFLOP/s | "
+             "frac of MFMA peak | algorithmic MB | GB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+    total = 0.0
+    for r in _stats_rows(trace_dir):
+        k = next((n for n in kernels if n in r["Name"]), None)
+        if k is None:
+            continue
+        avg, mn, mx = float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3
+        fl, by = work[k]
+        total += avg
+        lines.append(f"| {k} | {r['Calls']} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {fl / 1e9:.2f} | "
+                     f"{fl / (avg * 1e-6) / 1e12:.0f} | {fl / (avg * 1e-6) / 1e12 / peak_f:.3f} | "
+                     f"{by / 1e6:.1f} | {by / (avg * 1e-6) / 1e9:.0f} |")
+    T = case.tokens * len(case.blocks)
+    fl_step = flops_per_token(case.C, case.M * case.M) * T
+    lines += ["", f"Sum of the average durations per step ({len(case.blocks)} block(s)): "
+              f"{total * len(case.blocks):.1f} us -> {fl_step / (total * len(case.blocks) * 1e-6) / 1e12:.0f} "
+              f"TFLOP/s, {fl_step / (total * len(case.blocks) * 1e-6) / 1e12 / peak_f:.3f} of the "
+              f"{peak_f:.0f} TFLOP/s dense {case.dtype} peak."]
+    out = os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS",
+            "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE")
+
+
+def counters_summarize(name, pmc_dir, command):
+    """One rocprofv3 --pmc pass over COUNTERS -> profiles/counters_<workload>.md:
+    per kernel, matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over the
+    SIMDs x GPU cycles; GRBM_GUI_ACTIVE is reported once per XCD), instruction
+    mix per matrix-core instruction, and the share of wave time spent waiting."""
+    import collections
+    import workloads
+    import shifted_window_attention_roll_amd as swin
+    case = workloads.make_workload(name)
+    desc = swin.make_desc(case.B, case.H, case.W, case.C, case.heads, case.M,
+                          case.blocks[0].s, case.mode, case.torch_dtype)
+    kernels = swin.kernel_names(desc)
+    rows = _counter_rows(pmc_dir)
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    for r in rows:
+        k = next((n for n in kernels if n in r["Kernel_Name"]), None)
+        if k is None:
+            continue
+        acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+    simds = 4 * 256
+    lines = [f"# Counters, {name}", "", f"Command: `{command}`", "",
+             "Per launch (averaged over the launches of the run).  GPU cycles = "
+             "GRBM_GUI_ACTIVE / 8 (one count per XCD).  Matrix-core busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GPU cycles).", "",
+             "| kernel | launches | GPU cycles | MFMA instr | matrix-core busy | VALU / MFMA | "
+             "LDS / MFMA | wait share of wave cycles |", "|---|---|---|---|---|---|---|---|"]
+    for k in kernels:
+        if k not in acc:
+            continue
+        n = len(disp[k])
+        a = {c: v / n for c, v in acc[k].items()}
+        cyc = a.get("GRBM_GUI_ACTIVE", 0.0) / 8
+        mf = a.get("SQ_INSTS_MFMA", 0.0)
+        busy = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (simds * cyc) if cyc else float("nan")
+        lines.append(f"| {k} | {n} | {cyc:.0f} | {mf:.0f} | {busy:.3f} | "
+                     f"{a.get('SQ_INSTS_VALU', 0.0) / max(mf, 1):.2f} | "
+                     f"{a.get('SQ_INSTS_LDS', 0.0) / max(mf, 1):.2f} | "
+                     f"{a.get('SQ_WAIT_INST_ANY', 0.0) / max(a.get('SQ_WAVE_CYCLES', 1.0), 1):.3f} |")
+    out = os.path.join(ROOT, "profiles", f"counters_{name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -586,10 +721,21 @@ def main():
                     help="run --steps steps and the counter calibration copies, print no JSON")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc outputs into profiles/hbm_traffic.json")
+    ap.add_argument("--trace-summarize", metavar="TRACE_DIR",
+                    help="turn a rocprofv3 --kernel-trace --stats output into "
+                         "profiles/kernel_trace_<workload>.md")
+    ap.add_argument("--counters-summarize", metavar="PMC_DIR",
+                    help="turn a rocprofv3 --pmc output (COUNTERS) into profiles/counters_<workload>.md")
     ap.add_argument("--traffic-command", default="", help="command recorded with the summary")
     args = ap.parse_args()
     if args.traffic_summarize:
         traffic_summarize(args.workload, *args.traffic_summarize, args.traffic_command)
+        return
+    if args.trace_summarize:
+        trace_summarize(args.workload, args.trace_summarize, args.traffic_command)
+        return
+    if args.counters_summarize:
+        counters_summarize(args.workload, args.counters_summarize, args.traffic_command)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -14,8 +14,9 @@
  *
  * Geometry used throughout:
  *   x    [B, H, W, C] tokens, channels last.
- *   M    window side; a window holds N = M*M tokens; nW = (H/M)*(W/M) windows per
- *        image.  Requires H % M == 0 and W % M == 0.
+ *   M    window side, M >= 2; a window holds N = M*M tokens; nW = (H/M)*(W/M)
+ *        windows per image.  Requires H % M == 0 and W % M == 0 (else
+ *        SWIN_ERR_SHAPE).
  *   s    cyclic shift, 0 <= s < M.  Shifted-frame position (y', x') holds
  *        original position ((y'+s) mod H, (x'+s) mod W).
  *   Window w = b*nW + wy*(W/M) + wx; in-window token t = ty*M + tx; window
@@ -90,7 +91,8 @@ swin_status swin_reverse_unshift(const void* xw, void* x, int B, int H, int W, i
  *   table[r, h] = 16 * sigmoid( w2[h, :] . relu(w1 g + b1) + b2[h] )
  *   w1 [hidden, 2] (columns dy, dx), b1 [hidden], w2 [heads, hidden],
  *   b2 [heads] or NULL (no second bias); table [(2M-1)^2, heads].  All float32.
- * hidden in 1..4096, heads in 1..64, M in 1..32.
+ * hidden in 1..4096, heads in 1..64, M in 2..32 (else SWIN_ERR_SHAPE); table
+ * must not overlap an input (SWIN_ERR_ALIAS).
  */
 swin_status swin_cpb_table(const float* w1, const float* b1, const float* w2,
                            const float* b2, int hidden, int heads, int M,
@@ -125,8 +127,9 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d);
  *           (tx_i-tx_j+M-1).
  *   tau     [heads] float32, V2 only (raw; max(tau, tau_min) is used); may be
  *           NULL in V1.
- *   y       [B, H, W, C]   output, desc->dtype; must not overlap x or the
- *           workspace.
+ *   y       [B, H, W, C]   output, desc->dtype.  Neither y nor the workspace may
+ *           overlap any input (x, the weights, the biases, bias_table, tau) or
+ *           each other (SWIN_ERR_ALIAS).
  *   workspace, ws_bytes    at least swin_wmsa_workspace_size(desc) bytes.
  * Per window, with q, k, v the projections of the window's tokens:
  *   V1: logit(i,j) = scale * q_h(i).k_h(j) + table[idx(i,j), h]
@@ -185,7 +188,8 @@ swin_status swin_wmsa_fwd_timed(const swin_wmsa_desc* desc, const void* x, const
  * Parameters (device pointers, attn.dtype unless noted): the attention's as in
  * swin_wmsa_fwd; ln1_g, ln1_b, ln2_g, ln2_b [C]; fc1_w [hidden, C], fc1_b
  * [hidden] or NULL; fc2_w [C, hidden], fc2_b [C] or NULL.
- *   x, y [B, H, W, C]; y must not overlap x or the workspace.
+ *   x, y [B, H, W, C].  Neither y nor the workspace may overlap any input (x and
+ *   every parameter pointer) or each other (SWIN_ERR_ALIAS).
  *   workspace, ws_bytes >= swin_block_workspace_size(desc): the attention's
  *   workspace plus four intermediates (three [B*H*W, C], one [B*H*W, hidden]).
  * Requires a valid attention descriptor, hidden a multiple of 32 (<= 16384),
@@ -311,8 +315,8 @@ swin_status swin_fp8_linear(const unsigned char* a, const float* sa, const unsig
  *
  * swin_sparse24_linear: y [rows, N] = x [rows, K] wp^T + bias (dt, float32
  * accumulation), wp the dense matrix the compressed form describes; bias [N]
- * or NULL.  K a multiple of 64, N >= 1, rows >= 0 (SWIN_ERR_SHAPE); x and
- * values 16-byte, codes 4-byte aligned (SWIN_ERR_ALIGN); y must not overlap
+ * or NULL.  K a multiple of 64, N >= 1, rows >= 0 (SWIN_ERR_SHAPE); x, values
+ * and codes 16-byte aligned (SWIN_ERR_ALIGN); y must not overlap
  * an input (SWIN_ERR_ALIAS).
  */
 swin_status swin_sparse24_compress(const void* w, swin_dtype dt, int N, int K, void* values,

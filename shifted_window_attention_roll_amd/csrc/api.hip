@@ -25,7 +25,8 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 swin_status check_geometry(int B, int H, int W, int C, int M, int s) {
-  if (B < 0 || H < 1 || W < 1 || C < 1 || M < 1) return SWIN_ERR_SHAPE;
+  // A window holds at least 2 x 2 tokens.
+  if (B < 0 || H < 1 || W < 1 || C < 1 || M < 2) return SWIN_ERR_SHAPE;
   if (H % M || W % M) return SWIN_ERR_SHAPE;
   if (s < 0 || s >= M) return SWIN_ERR_SHAPE;
   if ((int64_t)B * H * W > INT32_MAX) return SWIN_ERR_UNSUPPORTED;
@@ -168,7 +169,7 @@ swin_status swin_cpb_table(const float* w1, const float* b1, const float* w2, co
                            int hidden, int heads, int M, float coord_scale, float* table,
                            void* stream) {
   if (!w1 || !b1 || !w2 || !table) return SWIN_ERR_NULL;
-  if (hidden < 1 || hidden > 4096 || heads < 1 || heads > 64 || M < 1 || M > 32)
+  if (hidden < 1 || hidden > 4096 || heads < 1 || heads > 64 || M < 2 || M > 32)
     return SWIN_ERR_SHAPE;
   const size_t tbytes = (size_t)(2 * M - 1) * (2 * M - 1) * heads * sizeof(float);
   if (overlap(table, tbytes, w1, (size_t)hidden * 2 * 4) || overlap(table, tbytes, b1, hidden * 4u) ||
@@ -235,11 +236,16 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
   const size_t e = elem_bytes(d->dtype);
   const size_t act = (size_t)d->B * d->H * d->W * d->C * e;
   const size_t C = d->C;
-  if (overlap(y, act, x, act) || overlap(y, act, workspace, L.total) ||
-      overlap(workspace, L.total, x, act) || overlap(y, act, w_qkv, 3 * C * C * e) ||
-      overlap(y, act, w_proj, C * C * e) || overlap(workspace, L.total, w_qkv, 3 * C * C * e) ||
-      overlap(workspace, L.total, w_proj, C * C * e))
-    return SWIN_ERR_ALIAS;
+  const size_t R2 = (size_t)(2 * d->M - 1) * (2 * d->M - 1);
+  // Neither the output nor the workspace may overlap any input, or each other.
+  struct Span { const void* p; size_t n; };
+  const Span ins[] = {{x, act}, {w_qkv, 3 * C * C * e}, {b_qkv, 3 * C * e},
+                      {w_proj, C * C * e}, {b_proj, C * e}, {bias_table, R2 * d->heads * 4},
+                      {d->mode == SWIN_V2 ? tau : nullptr, d->heads * 4u}};
+  for (const Span& in : ins)
+    if (overlap(y, act, in.p, in.n) || overlap(workspace, L.total, in.p, in.n))
+      return SWIN_ERR_ALIAS;
+  if (overlap(y, act, workspace, L.total)) return SWIN_ERR_ALIAS;
   if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(w_proj) || !aligned16(y) ||
       (L.total > 0 && !aligned16(workspace)))
     return SWIN_ERR_ALIGN;
@@ -509,8 +515,9 @@ swin_status swin_sparse24_linear(const void* x, const void* values, const unsign
   if (overlap(y, yb, x, (size_t)rows * K * 2) || overlap(y, yb, values, (size_t)N * K) ||
       overlap(y, yb, codes, (size_t)N * K / 4) || (bias && overlap(y, yb, bias, (size_t)N * 2)))
     return SWIN_ERR_ALIAS;
-  if (!aligned16(x) || !aligned16(values) || (reinterpret_cast<uintptr_t>(codes) & 3))
-    return SWIN_ERR_ALIGN;
+  // The tiled product reads the positions of 64 consecutive K with one
+  // 16-byte load per output channel.
+  if (!aligned16(x) || !aligned16(values) || !aligned16(codes)) return SWIN_ERR_ALIGN;
   Sparse24Linear p{x, values, codes, bias, y, rows, N, K};
   return from_hip(launch_sparse24_linear(p, io_of(dt), static_cast<hipStream_t>(stream)));
 }

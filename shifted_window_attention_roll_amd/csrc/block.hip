@@ -487,7 +487,7 @@ template <typename T, bool GELU, bool RES>
 hipError_t launch_dense(const T* A, const T* Wt, const T* bias, const T* R, T* Y, int rows, int N,
                         int K, hipStream_t st) {
   constexpr int io = __is_same(T, float) ? kF32 : __is_same(T, h16) ? kF16 : kBF16;
-  if (dense_tiled_supported(N, K, io)) {
+  if (dense_tiled_supported(rows, N, K, io)) {
     DenseParams d{io, rows, N, K, A, Wt, bias, RES ? R : nullptr, Y};
     return launch_dense_tiled(d, GELU, st);
   }
@@ -622,11 +622,20 @@ swin_status swin_block_fwd(const swin_block_desc* d, const void* x, const swin_b
   const size_t e = at.dtype == SWIN_F32 ? 4 : 2;
   const size_t act = (size_t)at.B * at.H * at.W * at.C * e;
   const size_t C = at.C, hid = d->hidden;
-  if (overlaps(y, act, x, act) || overlaps(y, act, workspace, L.total) ||
-      overlaps(workspace, L.total, x, act) || overlaps(y, act, p->fc1_w, hid * C * e) ||
-      overlaps(y, act, p->fc2_w, hid * C * e) || overlaps(workspace, L.total, p->fc1_w, hid * C * e) ||
-      overlaps(workspace, L.total, p->fc2_w, hid * C * e))
-    return SWIN_ERR_ALIAS;
+  const size_t R2 = (size_t)(2 * at.M - 1) * (2 * at.M - 1);
+  // Neither the output nor the workspace may overlap any input, or each other.
+  struct Span { const void* q; size_t n; };
+  const Span ins[] = {{x, act}, {p->w_qkv, 3 * C * C * e}, {p->b_qkv, 3 * C * e},
+                      {p->w_proj, C * C * e}, {p->b_proj, C * e},
+                      {p->bias_table, R2 * at.heads * 4},
+                      {at.mode == SWIN_V2 ? p->tau : nullptr, at.heads * 4u},
+                      {p->ln1_g, C * e}, {p->ln1_b, C * e}, {p->ln2_g, C * e}, {p->ln2_b, C * e},
+                      {p->fc1_w, hid * C * e}, {p->fc1_b, hid * e}, {p->fc2_w, hid * C * e},
+                      {p->fc2_b, C * e}};
+  for (const Span& in : ins)
+    if (overlaps(y, act, in.q, in.n) || overlaps(workspace, L.total, in.q, in.n))
+      return SWIN_ERR_ALIAS;
+  if (overlaps(y, act, workspace, L.total)) return SWIN_ERR_ALIAS;
   if (!al16(x) || !al16(y) || !al16(workspace) || !al16(p->fc1_w) || !al16(p->fc2_w) ||
       !al16(p->w_qkv) || !al16(p->w_proj) || !al16(p->ln1_g) || !al16(p->ln1_b) ||
       !al16(p->ln2_g) || !al16(p->ln2_b))

@@ -609,12 +609,15 @@ hipError_t dense_tiled_t(const DenseParams& d, bool gelu, hipStream_t st) {
 
 }  // namespace
 
-bool dense_tiled_supported(int N, int K, int io) {
-  return io != kF32 && N % 128 == 0 && (K == 256 || K == 512 || K == 1024 || K == 2048);
+// The operand buffer resources take 32-bit byte counts and offsets: A (rows x K,
+// 16-bit) must stay below 2 GiB.
+bool dense_tiled_supported(int64_t rows, int N, int K, int io) {
+  return io != kF32 && N % 128 == 0 && (K == 256 || K == 512 || K == 1024 || K == 2048) &&
+         rows * K * 2 < ((int64_t)1 << 31);
 }
 
 hipError_t launch_dense_tiled(const DenseParams& d, bool gelu, hipStream_t st) {
-  if (!dense_tiled_supported(d.N, d.K, d.io)) return hipErrorInvalidValue;
+  if (!dense_tiled_supported(d.rows, d.N, d.K, d.io)) return hipErrorInvalidValue;
   return d.io == kF16 ? dense_tiled_t<h16>(d, gelu, st) : dense_tiled_t<b16>(d, gelu, st);
 }
 

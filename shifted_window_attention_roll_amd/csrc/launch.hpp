@@ -70,7 +70,8 @@ struct DenseParams {
   const void* res;   // [rows, N] or null
   void* y;
 };
-bool dense_tiled_supported(int N, int K, int io);
+// rows * K * 2 must stay below 2^31 (32-bit buffer offsets); else the general kernel.
+bool dense_tiled_supported(int64_t rows, int N, int K, int io);
 hipError_t launch_dense_tiled(const DenseParams& d, bool gelu, hipStream_t st);
 
 bool tiled_gemm_supported(int C, int io);

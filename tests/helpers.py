@@ -74,3 +74,31 @@ def sample_windows(B: int, H: int, W: int, M: int, n_random: int, seed: int):
     rng = np.random.default_rng(seed)
     picks.update(int(v) for v in rng.integers(0, B * nW, n_random))
     return sorted(p for p in picks if 0 <= p < B * nW)
+
+
+def assert_block_close(y, ref, dtype, what):
+    """float32: the attention's bar (max-abs 1e-4).  16-bit: the block stores
+    its intermediates in the I/O type, so on top of the attention's bar (2e-2
+    absolute) each element carries (a) the rounding of h and of y, two
+    half-ulps of its own magnitude (half-ulp u = 2^-8 relative for bfloat16,
+    2^-11 for float16), and (b) roundings made before a LayerNorm or inside the
+    MLP (the attention output, a LayerNorm output, the hidden layer), which
+    scale with the token's RMS, about five such units; so per element
+    |err| <= 2e-2 + 2u |ref| + 5u RMS(ref row).  Overall rel-L2 <= 1e-2: the
+    attention sub-layer's own 5e-3 plus five stored roundings of about
+    u / (2 sqrt 3) RMS each (bfloat16: 1.1e-3; in quadrature 2.5e-3), with
+    margin."""
+    if dtype == "fp32":
+        assert_close(y, ref, dtype, what)
+        return
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
+    C = ref.shape[-1]
+    yr, rr = y.reshape(-1, C), ref.reshape(-1, C)
+    err = np.abs(yr - rr)
+    bound = 2e-2 + 2 * u * np.abs(rr) + 5 * u * np.sqrt((rr ** 2).mean(axis=1, keepdims=True))
+    i = int(np.argmax(err / bound))
+    assert np.all(err <= bound), f"{what}: |err| {err.flat[i]:.3e} > {bound.flat[i]:.3e}"
+    maxabs, rel = errors(y, ref)
+    assert rel <= 1e-2, f"{what}: rel-L2 {rel:.3e}"
+    return float(np.max(err / bound)), rel

@@ -73,10 +73,10 @@ FAKE = 1 << 20  # host-side stand-in addresses; validation fails before any use
 
 
 def _fwd(lib, d, x=FAKE, wq=FAKE * 2, wp=FAKE * 3, tab=FAKE * 4, tau=FAKE * 5, y=FAKE * 8,
-         ws=FAKE * 16, ws_bytes=None):
+         ws=FAKE * 16, ws_bytes=None, bq=None, bp=None):
     if ws_bytes is None:
         ws_bytes = lib.swin_wmsa_workspace_size(ctypes.byref(d))
-    return lib.swin_wmsa_fwd(ctypes.byref(d), x, wq, None, wp, None, tab, tau, y, ws, ws_bytes, None)
+    return lib.swin_wmsa_fwd(ctypes.byref(d), x, wq, bq, wp, bp, tab, tau, y, ws, ws_bytes, None)
 
 
 def test_fwd_rejects_before_launch(lib):
@@ -98,6 +98,17 @@ def test_fwd_rejects_before_launch(lib):
     assert _fwd(lib, small, y=FAKE + 64) == ALIAS             # y overlaps x
     assert _fwd(lib, small, ws=FAKE * 8 + 128) == ALIAS       # workspace overlaps y
     assert _fwd(lib, small, x=FAKE + 8) == ALIGN
+    # A window holds at least 2 x 2 tokens.
+    assert _fwd(lib, _desc(H=8, W=8, M=1, s=0)) == SHAPE
+    # Every input is checked against the output and the workspace.
+    v2 = _desc(B=1, H=16, W=16, C=160, heads=5, M=16, s=3, mode="v2")
+    assert _fwd(lib, small, tab=FAKE * 8 + 64) == ALIAS       # bias table inside y
+    assert _fwd(lib, small, tab=FAKE * 16 + 64) == ALIAS      # bias table inside the workspace
+    assert _fwd(lib, v2, tau=FAKE * 8 + 4) == ALIAS           # tau inside y
+    assert _fwd(lib, v2, tau=FAKE * 16 + 4) == ALIAS          # tau inside the workspace
+    assert _fwd(lib, small, bq=FAKE * 8 + 32) == ALIAS        # b_qkv inside y
+    assert _fwd(lib, small, bp=FAKE * 16 + 32) == ALIAS       # b_proj inside the workspace
+    assert _fwd(lib, small, wq=FAKE * 16 + 32) == ALIAS       # w_qkv inside the workspace
     assert lib.swin_wmsa_fwd(None, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, 0, None) == NULL
 
 
@@ -110,6 +121,7 @@ def test_index_maps_reject_before_launch(lib):
     assert f(FAKE, FAKE + 16, 1, 14, 14, 8, 7, 3, 1, None) == ALIAS
     assert f(FAKE + 2, FAKE * 4, 1, 14, 14, 8, 7, 3, 1, None) == ALIGN
     assert f(FAKE, FAKE * 4, 0, 14, 14, 8, 7, 3, 1, None) == OK
+    assert f(FAKE, FAKE * 4, 1, 14, 14, 8, 1, 0, 1, None) == SHAPE  # M < 2
     assert lib.swin_reverse_unshift(FAKE, FAKE * 4, 1, 14, 12, 8, 7, 3, 1, None) == SHAPE
 
 
@@ -119,6 +131,7 @@ def test_cpb_rejects_before_launch(lib):
     assert f(FAKE, FAKE * 2, FAKE * 3, None, 0, 4, 16, 0.0, FAKE * 8, None) == SHAPE
     assert f(FAKE, FAKE * 2, FAKE * 3, None, 512, 4, 33, 0.0, FAKE * 8, None) == SHAPE
     assert f(FAKE, FAKE * 2, FAKE * 3, None, 512, 4, 16, 0.0, FAKE + 64, None) == ALIAS
+    assert f(FAKE, FAKE * 2, FAKE * 3, None, 512, 4, 1, 0.0, FAKE * 8, None) == SHAPE  # M < 2
 
 
 def test_binding_refuses_cpu_tensors(lib):
@@ -204,6 +217,14 @@ def test_block_rejects_before_launch(lib):
     assert _block(lib, swin.make_block_desc(2, 56, 56, 96, 3, 7, 3, "v2"), tau=None) == NULL
     assert _block(lib, d, ws_bytes=64) == WS
     assert _block(lib, d, y=FAKE + 64) == ALIAS                              # y overlaps x
+    # every parameter is checked against y and the workspace
+    for name in [f[0] for f in swin.BlockParams._fields_]:
+        if name == "tau":
+            continue
+        assert _block(lib, d, **{name: FAKE * 8 + 16}) == ALIAS, name          # inside y
+        assert _block(lib, d, **{name: FAKE * 64 + 16}) == ALIAS, name         # inside the ws
+    dv2 = swin.make_block_desc(2, 56, 56, 96, 3, 7, 3, "v2", torch.float16)
+    assert _block(lib, dv2, tau=FAKE * 8 + 4) == ALIAS
     assert _block(lib, d, x=FAKE + 8) == ALIGN
     assert lib.swin_block_fwd(None, FAKE, None, FAKE, FAKE, 0, None) == NULL
 
@@ -269,3 +290,68 @@ def test_cpb_bwd_rejects_before_launch(lib):
     assert call(wsb=16) == WS
     assert call(dw2=F * 3 + 4) == ALIAS          # output over an input
     assert call(db1=F * 8 + 4) == ALIAS          # two outputs overlap
+
+
+def test_fp8_rejects_before_launch(lib):
+    q = lib.swin_fp8_quantize
+    assert q(FAKE, 9, 4, 64, FAKE * 4, FAKE * 8, None) == DTYPE
+    assert q(FAKE, 2, 4, 0, FAKE * 4, FAKE * 8, None) == SHAPE
+    assert q(FAKE, 2, 0, 64, FAKE * 4, FAKE * 8, None) == OK          # empty
+    assert q(None, 2, 4, 64, FAKE * 4, FAKE * 8, None) == NULL
+    assert q(FAKE, 2, 4, 64, FAKE + 16, FAKE * 8, None) == ALIAS      # codes inside x
+    assert q(FAKE + 8, 2, 4, 64, FAKE * 4, FAKE * 8, None) == ALIGN
+    f = lib.swin_fp8_linear
+    a = dict(a=FAKE, sa=FAKE * 2, w=FAKE * 3, sw=FAKE * 4, b=None, bdt=2, y=FAKE * 8, ydt=2,
+             rows=16, N=64, K=128)
+
+    def call(**kw):
+        v = dict(a)
+        v.update(kw)
+        return f(v["a"], v["sa"], v["w"], v["sw"], v["b"], v["bdt"], v["y"], v["ydt"], v["rows"],
+                 v["N"], v["K"], None)
+    assert call(ydt=9) == DTYPE
+    assert call(K=48) == SHAPE                   # K % 32
+    assert call(rows=0) == OK
+    assert call(sw=None) == NULL
+    assert call(y=FAKE * 3 + 64) == ALIAS        # y over the weight codes
+    assert call(b=FAKE * 8 + 16) == ALIAS        # bias inside y
+    assert call(w=FAKE * 3 + 4) == ALIGN
+
+
+def test_sparse24_rejects_before_launch(lib):
+    c = lib.swin_sparse24_compress
+    assert c(FAKE, 0, 64, 64, FAKE * 4, FAKE * 8, None) == DTYPE     # float32
+    assert c(FAKE, 2, 64, 66, FAKE * 4, FAKE * 8, None) == SHAPE     # K % 4
+    assert c(FAKE, 2, 0, 64, FAKE * 4, FAKE * 8, None) == OK
+    assert c(FAKE, 2, 64, 64, FAKE + 64, FAKE * 8, None) == ALIAS    # values inside w
+    f = lib.swin_sparse24_linear
+    a = dict(x=FAKE, v=FAKE * 2, c=FAKE * 3, b=None, y=FAKE * 8, dt=2, rows=16, N=64, K=128)
+
+    def call(**kw):
+        v = dict(a)
+        v.update(kw)
+        return f(v["x"], v["v"], v["c"], v["b"], v["y"], v["dt"], v["rows"], v["N"], v["K"], None)
+    assert call(dt=0) == DTYPE
+    assert call(K=96) == SHAPE                   # K % 64
+    assert call(rows=0) == OK
+    assert call(c=None) == NULL
+    assert call(y=FAKE * 2 + 64) == ALIAS        # y over the kept values
+    assert call(c=FAKE * 3 + 4) == ALIGN         # positions are read 16 bytes at a time
+    assert call(c=FAKE * 3 + 8) == ALIGN
+
+
+# Kernels the forward can enqueue, per plan: the parity cases with the tau clip
+# and the descriptor overrides (test_gpu_parity.PLAN_CASES) must reach each.
+PLAN_KERNELS = {"fused_w8_kernel", "fused_window_kernel", "fused_w16_kernel",
+                "tiled_attn_kernel", "w8_attn_kernel", "window_attn_kernel",
+                "qkv_tiled_kernel", "qkv_gemm_kernel", "proj_tiled_kernel", "proj_gemm_kernel"}
+
+
+def test_override_cases_cover_every_plan(lib):
+    from test_gpu_parity import PLAN_CASES
+    seen = set()
+    for (B, H, W, C, heads, M, s, dtype) in PLAN_CASES:
+        dt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[dtype]
+        for mode in ("v1", "v2"):
+            seen.update(swin.kernel_names(swin.make_desc(B, H, W, C, heads, M, s, mode, dt)))
+    assert seen == PLAN_KERNELS

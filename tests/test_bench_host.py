@@ -24,3 +24,18 @@ def test_digest_follows_includes():
     assert "attn_core.hpp" in _closure("tiled_attn_kernel")
     assert bench.source_digest("fused_w8_kernel") != bench.source_digest("tiled_attn_kernel")
     assert bench.source_digest("qkv_tiled_kernel") == bench.source_digest("proj_tiled_kernel")
+
+
+def test_cpu_sample_windows_cover_the_masked_edge():
+    # one 384 x 384 image, window 24: 256 windows; the sample spans the grid,
+    # first and last (masked) window included
+    w = bench._sample_windows(1, 384, 384, 24, 32)
+    assert w[0] == 0 and w[-1] == 255 and len(w) == 32
+    assert bench._sample_windows(1, 48, 48, 24, 99) == [0, 1, 2, 3]
+
+
+def test_headline_is_the_largest_single_gpu_workload():
+    import workloads
+    flops = {n: bench.flops_per_token(w["C"], w["M"] ** 2) * w["B"] * w["H"] * w["W"] *
+             len(w["shifts"]) for n, w in workloads.WORKLOADS.items()}
+    assert bench.MAIN == max(flops, key=flops.get)

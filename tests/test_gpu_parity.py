@@ -1,5 +1,5 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle on seeded
-inputs.  Index maps bit-exact; CPB table within 1e-5; the block forward within
+inputs (the five workloads compared on every output element).  Index maps bit-exact; CPB table within 1e-5; the block forward within
 max-abs 1e-4 (float32) or max-abs 2e-2 and relative L2 5e-3 (fp16 / bf16)."""
 import sys
 
@@ -215,43 +215,130 @@ def test_wmsa_deterministic_and_every_output_written(gpu, B, H, W, C, heads, M, 
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-# --- the five workloads at full size --------------------------------------------
+# --- tau clip and descriptor overrides, in every plan -------------------------
 
-def _workload_parity(gpu, name, n_random, full=False):
+# One shape per kernel plan (the kernel names each case takes are listed by
+# test_abi.py::test_override_cases_cover_every_plan, which runs without a GPU).
+PLAN_CASES = [
+    # B, H, W, C, heads, M, s, dtype
+    (2, 14, 14, 96, 3, 7, 3, "bf16"),     # fused window 7
+    (2, 16, 16, 128, 4, 8, 4, "fp16"),    # fused window 8, 4 heads
+    (1, 12, 12, 64, 2, 6, 3, "bf16"),     # fused small window
+    (1, 10, 10, 64, 2, 5, 2, "fp32"),     # fused small window, float32
+    (2, 32, 32, 128, 4, 16, 8, "bf16"),   # fused window 16
+    (1, 32, 32, 160, 5, 16, 8, "bf16"),   # tiled attention between the GEMMs, window 16
+    (1, 48, 48, 96, 3, 24, 12, "bf16"),   # tiled attention, window 24
+    (1, 48, 48, 512, 16, 24, 12, "bf16"),  # window 24 with C = 512 (tiled GEMMs)
+    (1, 16, 24, 256, 8, 8, 4, "fp16"),    # tiled attention, window 8, tiled GEMMs
+    (1, 14, 21, 192, 6, 7, 3, "bf16"),    # window 7 between the GEMMs
+    (1, 24, 24, 160, 5, 12, 6, "bf16"),   # general three kernels
+    (1, 32, 32, 64, 2, 16, 8, "fp32"),    # general three kernels, float32
+]
+
+# Raw tau per head: several below the 0.01 clip (1/tau up to 2000 if a kernel
+# dropped it), one at it, others above.
+TAU_RAW = [0.002, 0.0099, 0.04, 0.0005, 0.01, 0.2, 0.006, 0.08, 0.003, 0.05, 0.001, 0.03,
+           0.0001, 0.015, 0.007, 0.1]
+
+
+def _override_run(gpu, B, H, W, C, heads, M, s, dtype, mode, tau=None, scale=0.0, tau_min=0.0):
+    case = workloads.make_case(B, H, W, C, heads, M, (s,), dtype, mode, seed=31 * M + heads + s,
+                               w_std=0.08, bias_std=0.1, tau="uniform")
+    blk = case.blocks[0]
+    if tau is not None:
+        blk.tau = torch.tensor(tau[:heads], dtype=torch.float32)
+    dev = "cuda"
+    x = case.x.to(dev)
+    out = torch.full_like(x, float("nan"))
+    y = gpu.wmsa_fwd(x, blk.w_qkv.to(dev), blk.b_qkv.to(dev), blk.w_proj.to(dev),
+                     blk.b_proj.to(dev), helpers.gpu_table(case, blk, dev), M, s, heads, mode,
+                     tau=None if blk.tau is None else blk.tau.to(dev), scale=scale,
+                     tau_min=tau_min, out=out)
+    torch.cuda.synchronize()
+    # The descriptor carries float32 scale / tau_min: hand the oracle the same values.
+    kw = {}
+    if scale > 0:
+        kw["scale"] = float(np.float32(scale))
+    if tau_min > 0:
+        kw["tau_min"] = float(np.float32(tau_min))
+    ref = so.wmsa_forward(workloads.f64(case.x), workloads.f64(blk.w_qkv),
+                          workloads.f64(blk.b_qkv), workloads.f64(blk.w_proj),
+                          workloads.f64(blk.b_proj), helpers.oracle_table(case, blk), M, s, heads,
+                          mode, tau=None if blk.tau is None else workloads.f64(blk.tau), **kw)
+    return workloads.f64(y.cpu()), ref
+
+
+@pytest.mark.parametrize("B,H,W,C,heads,M,s,dtype", PLAN_CASES)
+def test_wmsa_v2_tau_below_clip(gpu, B, H, W, C, heads, M, s, dtype):
+    """"Swin Transformer V2" summary, How It Works: tau is clipped at 0.01."""
+    _say(f"tau clip B={B} H={H} W={W} C={C} heads={heads} M={M} s={s} {dtype}")
+    got, ref = _override_run(gpu, B, H, W, C, heads, M, s, dtype, "v2", tau=TAU_RAW)
+    helpers.assert_close(got, ref, dtype, "tau clip")
+
+
+@pytest.mark.parametrize("B,H,W,C,heads,M,s,dtype", PLAN_CASES)
+def test_wmsa_v2_tau_min_override(gpu, B, H, W, C, heads, M, s, dtype):
+    _say(f"tau_min B={B} H={H} W={W} C={C} heads={heads} M={M} s={s} {dtype}")
+    got, ref = _override_run(gpu, B, H, W, C, heads, M, s, dtype, "v2", tau=TAU_RAW,
+                             tau_min=0.05)
+    helpers.assert_close(got, ref, dtype, "tau_min 0.05")
+
+
+@pytest.mark.parametrize("B,H,W,C,heads,M,s,dtype", PLAN_CASES)
+def test_wmsa_v1_scale_override(gpu, B, H, W, C, heads, M, s, dtype):
+    _say(f"scale B={B} H={H} W={W} C={C} heads={heads} M={M} s={s} {dtype}")
+    got, ref = _override_run(gpu, B, H, W, C, heads, M, s, dtype, "v1", scale=0.37)
+    helpers.assert_close(got, ref, dtype, "scale 0.37")
+
+
+# --- the five workloads at full size: every output element ---------------------
+
+def _workload_parity(gpu, name):
     case = workloads.make_workload(name)
     x = case.x.cuda()
     x_host = case.x
     for bi, blk in enumerate(case.blocks):
         _say(f"workload {name} block {bi} s={blk.s}")
-        y = helpers.run_gpu_block(case, blk, x)
+        out = torch.full_like(x, float("nan"))  # every element must be written
+        y = helpers.run_gpu_block(case, blk, x, out=out)
         y_host = y.cpu()
-        x64 = workloads.f64(x_host)
-        if full:
-            ref = helpers.run_oracle_block(case, blk, x64)
-            got = workloads.f64(y_host)
-        else:
-            wins = helpers.sample_windows(case.B, case.H, case.W, case.M, n_random, seed=bi + 11)
-            tok, ref = helpers.run_oracle_block(case, blk, x64, windows=wins)
-            got = workloads.f64(y_host).reshape(-1, case.C)[tok]
-        helpers.assert_close(got, ref, case.dtype, f"{name} block {bi}")
+        ref = helpers.run_oracle_block(case, blk, workloads.f64(x_host))
+        helpers.assert_close(workloads.f64(y_host), ref, case.dtype, f"{name} block {bi}")
         x, x_host = y, y_host  # the next block consumes this block's output
 
 
-def test_workload_swin_t_stage1_b1_fp32_full(gpu):
-    _workload_parity(gpu, "swin_t_stage1_b1_fp32", 0, full=True)
+def test_workload_swin_t_stage1_b1_fp32(gpu):
+    _workload_parity(gpu, "swin_t_stage1_b1_fp32")
 
 
 def test_workload_swin_t_stage1_b64_fp16(gpu):
-    _workload_parity(gpu, "swin_t_stage1_b64_fp16", 24)
+    _workload_parity(gpu, "swin_t_stage1_b64_fp16")
 
 
 def test_workload_swin_b_stage3_b64_bf16(gpu):
-    _workload_parity(gpu, "swin_b_stage3_b64_bf16", 24)
+    _workload_parity(gpu, "swin_b_stage3_b64_bf16")
 
 
 def test_workload_swinv2_b_stage1_w16_bf16(gpu):
-    _workload_parity(gpu, "swinv2_b_stage1_w16_bf16", 16)
+    _workload_parity(gpu, "swinv2_b_stage1_w16_bf16")
 
 
 def test_workload_swinv2_g_stage1_384_w24_bf16(gpu):
-    _workload_parity(gpu, "swinv2_g_stage1_384_w24_bf16", 12)
+    _workload_parity(gpu, "swinv2_g_stage1_384_w24_bf16")
+
+
+@pytest.mark.parametrize("name", ["swin_b_stage3_b64_bf16", "swinv2_g_stage1_384_w24_bf16"])
+def test_workload_deterministic(gpu, name):
+    """Two runs of a three-kernel plan at full size into NaN-filled outputs:
+    bit-identical, every element written."""
+    _say(f"determinism {name}")
+    case = workloads.make_workload(name)
+    blk = case.blocks[0]
+    x = case.x.cuda()
+    out = torch.full_like(x, float("nan"))
+    y1 = helpers.run_gpu_block(case, blk, x, out=out).clone()
+    out.fill_(float("nan"))
+    y2 = helpers.run_gpu_block(case, blk, x, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1.float()).all()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
