@@ -42,7 +42,9 @@ def _same_as_first(y):
 
 
 def test_beyond_2gib(gpu):
-    case = workloads.make_case(1, H, W, C, HEADS, M, (S,), "bf16", "v2", seed=88, w_std=0.08,
+    # Weights N(0, 0.02^2), the recipe of the C = 512 workloads (larger weights
+    # put outputs near 16, where one bfloat16 rounding exceeds the 2e-2 bar).
+    case = workloads.make_case(1, H, W, C, HEADS, M, (S,), "bf16", "v2", seed=88, w_std=0.02,
                                bias_std=0.05, tau="uniform")
     blk = case.blocks[0]
     dev = "cuda"

@@ -241,9 +241,14 @@ TAU_RAW = [0.002, 0.0099, 0.04, 0.0005, 0.01, 0.2, 0.006, 0.08, 0.003, 0.05, 0.0
            0.0001, 0.015, 0.007, 0.1]
 
 
-def _override_run(gpu, B, H, W, C, heads, M, s, dtype, mode, tau=None, scale=0.0, tau_min=0.0):
+def _override_run(gpu, B, H, W, C, heads, M, s, dtype, mode, tau=None, scale=0.0, tau_min=0.0,
+                  w_std=None):
+    # C = 512: weights N(0, 0.02^2) as in the C = 512 workloads (N(0, 0.08^2) would
+    # put outputs near 16, past what the 2e-2 absolute bar allows a bfloat16 value).
+    if w_std is None:
+        w_std = 0.08 if C < 512 else 0.02
     case = workloads.make_case(B, H, W, C, heads, M, (s,), dtype, mode, seed=31 * M + heads + s,
-                               w_std=0.08, bias_std=0.1, tau="uniform")
+                               w_std=w_std, bias_std=0.1, tau="uniform")
     blk = case.blocks[0]
     if tau is not None:
         blk.tau = torch.tensor(tau[:heads], dtype=torch.float32)
@@ -287,7 +292,10 @@ def test_wmsa_v2_tau_min_override(gpu, B, H, W, C, heads, M, s, dtype):
 @pytest.mark.parametrize("B,H,W,C,heads,M,s,dtype", PLAN_CASES)
 def test_wmsa_v1_scale_override(gpu, B, H, W, C, heads, M, s, dtype):
     _say(f"scale B={B} H={H} W={W} C={C} heads={heads} M={M} s={s} {dtype}")
-    got, ref = _override_run(gpu, B, H, W, C, heads, M, s, dtype, "v1", scale=0.37)
+    # A logit multiplier twice the default (d^-1/2 = 0.177); weights N(0, 0.05^2)
+    # keep the sharper softmax's outputs within the absolute bar's range.
+    got, ref = _override_run(gpu, B, H, W, C, heads, M, s, dtype, "v1", scale=0.37,
+                             w_std=0.05 if C < 512 else 0.02)
     helpers.assert_close(got, ref, dtype, "scale 0.37")
 
 
