@@ -42,7 +42,9 @@ typedef enum {
   SWIN_ERR_ALIAS = 5,       /* an output overlaps an input or the workspace        */
   SWIN_ERR_WORKSPACE = 6,   /* workspace smaller than swin_wmsa_workspace_size()   */
   SWIN_ERR_ALIGN = 7,       /* a pointer is not 16-byte aligned                    */
-  SWIN_ERR_HIP = 8          /* the HIP runtime reported an error at launch         */
+  SWIN_ERR_HIP = 8,         /* the HIP runtime reported an error at launch         */
+  SWIN_ERR_SCRATCH = 9      /* swin_wmsa_fwd_noalloc: the call needs more scratch
+                               than SWIN_NOALLOC_SCRATCH_BYTES                      */
 } swin_status;
 
 typedef enum { SWIN_F32 = 0, SWIN_F16 = 1, SWIN_BF16 = 2 } swin_dtype;
@@ -169,6 +171,28 @@ swin_status swin_wmsa_fwd_timed(const swin_wmsa_desc* desc, const void* x, const
                                 const float* bias_table, const float* tau, void* y,
                                 void* workspace, size_t ws_bytes, void* stream,
                                 void* const* events, int n_events);
+
+/*
+ * swin_wmsa_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * workspace is the library's own fixed device array of
+ * SWIN_NOALLOC_SCRATCH_BYTES per GPU (a file-scope static, held by every GPU the
+ * library runs on until the process ends), instead of a caller buffer.  Same
+ * arguments (minus workspace / ws_bytes), validation, kernels and results as
+ * swin_wmsa_fwd; the caller still passes inputs and outputs.  A descriptor
+ * whose swin_wmsa_workspace_size exceeds SWIN_NOALLOC_SCRATCH_BYTES returns
+ * SWIN_ERR_SCRATCH and launches nothing.  Nothing here calls hipMalloc / hipFree
+ * or an allocating library routine; the array's device address is looked up
+ * (hipGetSymbolAddress) on the first call on each device, with that device
+ * current.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind: calls that may overlap on one GPU (several streams or
+ * threads) race and must be serialised by the caller.
+ */
+#define SWIN_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+swin_status swin_wmsa_fwd_noalloc(const swin_wmsa_desc* desc, const void* x, const void* w_qkv,
+                                  const void* b_qkv, const void* w_proj, const void* b_proj,
+                                  const float* bias_table, const float* tau, void* y,
+                                  void* stream);
 
 /*
  * Full block forward around the attention sub-layer.

@@ -25,7 +25,7 @@ _EXPORTS = ("swin_status_str", "swin_abi_version", "swin_partition_shift", "swin
             "swin_block_workspace_size", "swin_block_fwd", "swin_wmsa_bwd_workspace_size",
             "swin_wmsa_bwd", "swin_cpb_bwd_workspace_size", "swin_cpb_bwd",
             "swin_fp8_quantize", "swin_fp8_linear", "swin_sparse24_compress",
-            "swin_sparse24_linear")
+            "swin_sparse24_linear", "swin_wmsa_fwd_noalloc")
 
 
 class SwinDesc(ctypes.Structure):
@@ -82,6 +82,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.swin_wmsa_fwd_timed.argtypes = [ctypes.POINTER(SwinDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                         vp, ctypes.c_size_t, vp, ctypes.POINTER(vp), i]
     lib.swin_wmsa_kernel_count.restype = i
+    lib.swin_wmsa_fwd_noalloc.restype = st
+    lib.swin_wmsa_fwd_noalloc.argtypes = [ctypes.POINTER(SwinDesc), vp, vp, vp, vp, vp, vp, vp,
+                                          vp, vp]
     lib.swin_wmsa_kernel_count.argtypes = [ctypes.POINTER(SwinDesc)]
     lib.swin_wmsa_kernel_name.restype = ctypes.c_char_p
     lib.swin_wmsa_kernel_name.argtypes = [ctypes.POINTER(SwinDesc), i]
@@ -215,6 +218,27 @@ def wmsa_fwd(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv: Optional[torch.Tensor]
     else:
         arr = (ctypes.c_void_p * len(events))(*events)
         _check(lib.swin_wmsa_fwd_timed(*args, arr, len(events)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 160 << 20
+
+
+def wmsa_fwd_noalloc(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv: Optional[torch.Tensor],
+                     w_proj: torch.Tensor, b_proj: Optional[torch.Tensor],
+                     bias_table: torch.Tensor, M: int, s: int, heads: int, mode: str = "v1",
+                     tau: Optional[torch.Tensor] = None, scale: float = 0.0,
+                     tau_min: float = 0.0, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """wmsa_fwd through swin_wmsa_fwd_noalloc: the library's fixed device scratch
+    serves as the workspace (pass ``out`` to allocate nothing at all)."""
+    B, H, W, C = x.shape
+    desc = make_desc(B, H, W, C, heads, M, s, mode, x.dtype, scale, tau_min)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(load_library().swin_wmsa_fwd_noalloc(
+        ctypes.byref(desc), _ptr(x), _ptr(w_qkv), _ptr(b_qkv), _ptr(w_proj), _ptr(b_proj),
+        _ptr(bias_table), _ptr(tau), _ptr(out), _stream(stream)))
     return out
 
 

@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "swin_wmsa.h"
 #include "launch.hpp"
 
@@ -132,6 +134,9 @@ const char* swin_status_str(swin_status s) {
     case SWIN_ERR_WORKSPACE: return "SWIN_ERR_WORKSPACE: workspace too small";
     case SWIN_ERR_ALIGN: return "SWIN_ERR_ALIGN: pointer not 16-byte aligned";
     case SWIN_ERR_HIP: return "SWIN_ERR_HIP: the HIP runtime reported an error";
+    case SWIN_ERR_SCRATCH:
+      return "SWIN_ERR_SCRATCH: the call needs more than the no-alloc entry point's fixed "
+             "scratch (SWIN_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown swin_status";
 }
@@ -316,6 +321,53 @@ swin_status swin_wmsa_fwd_timed(const swin_wmsa_desc* d, const void* x, const vo
   if (!events) return SWIN_ERR_NULL;
   return wmsa_forward(d, x, w_qkv, b_qkv, w_proj, b_proj, bias_table, tau, y, workspace,
                       ws_bytes, stream, events, n_events);
+}
+
+// ---------------------------------------------------------------------------
+// No-allocation forward: the workspace is this file-scope device array.  In
+// host code `scratch` names a host-side stand-in, never its device address:
+// kernels and copies only ever get the address hipGetSymbolAddress returns,
+// kept per device.
+
+static __device__ __attribute__((aligned(256))) unsigned char scratch[SWIN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch` (looked up once per
+// device, with that device current).
+swin_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SWIN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SWIN_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SWIN_OK;
+}
+}  // namespace
+
+swin_status swin_wmsa_fwd_noalloc(const swin_wmsa_desc* d, const void* x, const void* w_qkv,
+                                  const void* b_qkv, const void* w_proj, const void* b_proj,
+                                  const float* bias_table, const float* tau, void* y,
+                                  void* stream) {
+  swin_status st = validate_desc(d);
+  if (st != SWIN_OK) return st;
+  if (d->B == 0) return SWIN_OK;
+  const size_t need = ws_layout(d).total;
+  if (need > SWIN_NOALLOC_SCRATCH_BYTES) return SWIN_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != SWIN_OK) return st;
+  }
+  return wmsa_forward(d, x, w_qkv, b_qkv, w_proj, b_proj, bias_table, tau, y, ws,
+                      need > 0 ? (size_t)SWIN_NOALLOC_SCRATCH_BYTES : 0, stream, nullptr, 0);
 }
 
 }  // extern "C"

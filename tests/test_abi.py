@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.swin_abi_version() == 1
-    for code in range(9):
+    for code in range(10):
         s = lib.swin_status_str(code).decode()
         assert s.startswith("SWIN_")
     assert lib.swin_status_str(99).decode() == "unknown swin_status"
@@ -355,3 +355,16 @@ def test_override_cases_cover_every_plan(lib):
         for mode in ("v1", "v2"):
             seen.update(swin.kernel_names(swin.make_desc(B, H, W, C, heads, M, s, mode, dt)))
     assert seen == PLAN_KERNELS
+
+
+def test_noalloc_rejects_before_launch(lib):
+    f = lib.swin_wmsa_fwd_noalloc
+    big = _desc(B=64, H=384, W=384, C=512, heads=16, M=24, s=12, dtype=torch.bfloat16)
+    assert lib.swin_wmsa_workspace_size(ctypes.byref(big)) > swin.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), FAKE, FAKE * 2, None, FAKE * 3, None, FAKE * 4, None, FAKE * 8,
+             None) == 9                                          # SWIN_ERR_SCRATCH
+    assert f(ctypes.byref(_desc(H=50)), FAKE, FAKE * 2, None, FAKE * 3, None, FAKE * 4, None,
+             FAKE * 8, None) == SHAPE
+    assert f(ctypes.byref(_desc(B=0)), FAKE, FAKE * 2, None, FAKE * 3, None, FAKE * 4, None,
+             FAKE * 8, None) == OK
+    assert f(None, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE, None) == NULL
