@@ -67,7 +67,14 @@ int qk_type(const swin_wmsa_desc* d) {
 // few heads and 16-bit I/O; else the QKV GEMM -> window
 // attention -> projection GEMM sequence through the workspace, with the tiled
 // attention (chunked slots) for 16-bit I/O and window sides 8, 16, 24.
-enum Plan { kPlanFusedSmall = 0, kPlanThree = 1, kPlanTiled = 2, kPlanFusedW16 = 3, kPlanFusedW8 = 4 };
+enum Plan {
+  kPlanFusedSmall = 0,
+  kPlanThree = 1,
+  kPlanTiled = 2,
+  kPlanFusedW16 = 3,
+  kPlanFusedW8 = 4,
+  kPlanFusedQkv = 5  // QKV + attention in one kernel, then the projection GEMM
+};
 
 int io_type(const swin_wmsa_desc* d) {
   return d->dtype == SWIN_F32 ? kF32 : d->dtype == SWIN_F16 ? kF16 : kBF16;
@@ -78,6 +85,8 @@ Plan choose_plan(const swin_wmsa_desc* d) {
   if (fused_w8_supported(d->M, d->C, heads, io_type(d))) return kPlanFusedW8;
   if (d->M * d->M <= 64 && heads <= 4 && d->C == kHeadDim * heads) return kPlanFusedSmall;
   if (fused_w16_supported(d->M, d->C, heads, io_type(d))) return kPlanFusedW16;
+  if (fused_qkv_attn_supported((int64_t)d->B * d->H * d->W, d->M, d->C, heads, io_type(d)))
+    return kPlanFusedQkv;
   if (tiled_attn_supported(d->M, io_type(d))) return kPlanTiled;
   return kPlanThree;
 }
@@ -98,6 +107,12 @@ WsLayout ws_layout(const swin_wmsa_desc* d) {
   const size_t tokens = (size_t)d->B * d->H * d->W;
   const size_t e = elem_bytes(d->dtype);
   const size_t eq = qk_type(d) == kF32 ? 4 : 2;
+  if (plan == kPlanFusedQkv) {  // O, then the redo flags (L.q marks their offset)
+    const size_t o = round_up(tokens * d->C * e, 256);
+    const size_t items = (size_t)d->B * (d->H / d->M) * (d->W / d->M) * d->heads;
+    return WsLayout{o, 0, 0, 0,
+                    o + round_up((size_t)fused_qkv_attn_flag_count(d->M, items) * 4, 256)};
+  }
   WsLayout L;
   L.q = 0;
   L.k = round_up(L.q + tokens * d->C * eq, 256);
@@ -191,7 +206,7 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
   return ws_layout(d).total;
 }
 
-static const int kPlanCount[5] = {1, 3, 3, 1, 1};
+static const int kPlanCount[6] = {1, 3, 3, 1, 1, 3};
 
 static const char* stage_name(const swin_wmsa_desc* d, int i) {
   const Plan plan = choose_plan(d);
@@ -199,6 +214,11 @@ static const char* stage_name(const swin_wmsa_desc* d, int i) {
   if (plan == kPlanFusedW16) return "fused_w16_kernel";
   if (plan == kPlanFusedW8) return "fused_w8_kernel";
   const bool tg = use_tiled_gemm(d);
+  if (plan == kPlanFusedQkv)
+    return i == 0   ? "fused_qkv_attn_kernel"
+           : i == 1 ? "fused_qkv_attn_redo_kernel"
+           : tg     ? "proj_tiled_kernel"
+                    : "proj_gemm_kernel";
   if (i == 0) return tg ? "qkv_tiled_kernel" : "qkv_gemm_kernel";
   if (i == 1)
     return plan == kPlanTiled                         ? "tiled_attn_kernel"
@@ -259,7 +279,7 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
   memset(&p, 0, sizeof(p));
   p.g = make_geom(d->B, d->H, d->W, d->C, d->M, d->s, d->heads);
   p.io = io_type(d);
-  p.g.chunked = (plan == kPlanTiled || plan == kPlanFusedW16) ? 1 : 0;
+  p.g.chunked = (plan == kPlanTiled || plan == kPlanFusedW16 || plan == kPlanFusedQkv) ? 1 : 0;
   p.qk = qk_type(d);
   p.v2 = d->mode == SWIN_V2;
   const float scale = d->scale > 0.0f ? d->scale : 1.0f / sqrtf((float)kHeadDim);
@@ -293,6 +313,17 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
     return from_hip(err);
   }
   const bool tg = use_tiled_gemm(d);
+  if (plan == kPlanFusedQkv) {
+    int* flags = reinterpret_cast<int*>(ws + L.q);
+    p.buf.o = ws;
+    if (err == hipSuccess) err = launch_fused_qkv_attn(p, flags, false, hs);
+    if (err == hipSuccess) err = mark(1);
+    if (err == hipSuccess) err = launch_fused_qkv_attn(p, flags, true, hs);
+    if (err == hipSuccess) err = mark(2);
+    if (err == hipSuccess) err = tg ? launch_proj_tiled(p, hs) : launch_proj_gemm(p, hs);
+    if (err == hipSuccess) err = mark(3);
+    return from_hip(err);
+  }
   if (err == hipSuccess) err = tg ? launch_qkv_tiled(p, hs) : launch_qkv_gemm(p, hs);
   if (err == hipSuccess) err = mark(1);
   if (err == hipSuccess)

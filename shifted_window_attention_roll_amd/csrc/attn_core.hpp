@@ -71,15 +71,22 @@ __device__ __forceinline__ void fill_bias_table(float* rt, const float* table, i
   }
 }
 
-// Softmax reference of the unmasked windows (masked windows, and the fallback
-// of the fixed schemes, always use the lazy one):
+// Softmax reference:
 //   kLazy   -- moves lazily, one compare and ballot per key block;
-//   kBlock0 -- block 0's row max, fixed;
-//   kZero   -- 0, fixed (bfloat16 P only): the caller has shifted the head's
-//              bias table by a constant so that no logit (base 2) exceeds
-//              kZeroTop; no max and no subtraction at all.
-// The fixed schemes check the row sums once at the end.
-enum class RefMode { kLazy, kBlock0, kZero };
+//   kBlock0 -- block 0's row max, fixed (unmasked windows only: a masked row
+//              may have no allowed key in block 0; masked windows then run
+//              kLazy);
+//   kZero   -- 0, fixed (bfloat16 P only; masked windows too): the caller has
+//              shifted the head's bias table by a constant so that no logit
+//              (base 2) exceeds kZeroTop; no max and no subtraction at all;
+//   kOwn    -- fixed, per tile the row max over the tile's own key block (the
+//              32 slots that hold its 16 queries: every row has its own token
+//              there, always allowed, so the reference is a logit of the row
+//              and every row sum is at least 1); masked windows too, at the
+//              cost of two more products per tile.
+// The fixed schemes check the row sums once at the end (the fallback of all
+// of them is the lazy pass).
+enum class RefMode { kLazy, kBlock0, kZero, kOwn };
 constexpr float kZeroTop = 64.0f;
 
 struct NoHook {
@@ -118,10 +125,10 @@ __device__ __forceinline__ void fill_bias_copies(float* rt4, const float* table,
 // O for the lane's query and d = 8*(l/16) + e, e = 0..7.  LAYOUT / TABLE pick
 // the K, V layout and the bias-table mode; hook(kbi) runs at the start of key
 // block kbi (the caller's work to interleave, e.g. staging the next item).
-// With a fixed reference and !MASKED, returns false (o undefined) when the
-// row sums show that some P left the safe range; the caller then runs the
-// MASKED instance with my = mx = false, which is exact for any logits.
-// Otherwise returns true.
+// With a fixed reference (kZero, kOwn, or kBlock0 and !MASKED), returns false
+// (o undefined) when the row sums show that some P left the safe range; the
+// caller then runs the MASKED kLazy instance (with the window's my / mx),
+// which is exact for any logits.  Otherwise returns true.
 template <typename QT, typename VT, int M, int QTL, bool MASKED,
           KvLayout LAYOUT = KvLayout::kPadded, TableMode TABLE = TableMode::kTable4,
           RefMode REF = RefMode::kBlock0, class Hook = NoHook>
@@ -171,7 +178,7 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     else
       tb[j] = (lds_f4)(rt4 + (a0 & 3) * TS + (a0 & ~3));
     o0[j] = o1[j] = ls[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[j] = (REF == RefMode::kZero && !MASKED) ? 0.0f : -1e30f;
+    m[j] = REF == RefMode::kZero ? 0.0f : -1e30f;
     mt[j] = -1e30f;
   }
   vec8<VT> ones;
@@ -254,6 +261,32 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     }
   };
 
+  if constexpr (REF == RefMode::kOwn) {
+#pragma unroll
+    for (int j = 0; j < QTL; ++j) {
+      const int kbo = tile[j] >> 1;  // the key block holding the tile's slots
+      Ops op;
+      load_kv(kbo, op);
+      load_bias(kbo, op);
+      f32x4 s0 = op.b0[j], s1 = op.b1[j];
+      if constexpr (MASKED) {
+        const int left = min(max(bnd - 8 * (kbo / BPC), 0), 8);
+        if (mx && left > 0 && left < 8) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (!((op.bits[j] >> r) & 1u)) s0[r] = NEG_INF;
+            if (!((op.bits[j] >> (4 + r)) & 1u)) s1[r] = NEG_INF;
+          }
+        }
+      }
+      s0 = mma_16x16x32(op.k0, qf[j], s0);
+      s1 = mma_16x16x32(op.k1, qf[j], s1);
+      const float bm = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                             fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+      m[j] = xor32_max(xor16_max(bm));
+    }
+  }
+
   Ops cur;
   load_kv(0, cur);
   if constexpr (!T1) load_bias(0, cur);
@@ -285,7 +318,8 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     }
     // Phase 1, every tile: S^T = K Q^T on top of the bias, block max (with
     // the fixed reference, only in block 0).
-    constexpr bool FIXED = REF != RefMode::kLazy && !MASKED;
+    constexpr bool FIXED = REF == RefMode::kZero || REF == RefMode::kOwn ||
+                           (REF == RefMode::kBlock0 && !MASKED);
     constexpr bool BLOCK0 = FIXED && REF == RefMode::kBlock0;
     f32x4 s0[QTL], s1[QTL];
     float bm[QTL];
@@ -355,7 +389,8 @@ __device__ __forceinline__ bool attn_tiles(const vec8<QT> (&qf)[QTL], const int 
     if (kbi + 1 < NB) cur = nxt;
   }
 
-  if constexpr (REF != RefMode::kLazy && !MASKED) {
+  if constexpr (REF == RefMode::kZero || REF == RefMode::kOwn ||
+                (REF == RefMode::kBlock0 && !MASKED)) {
     // Every P is at most its row sum.  A row sum below kFixedLimit (also
     // false for inf / NaN) means no P went past it: bfloat16 P stays far
     // from its overflow, float16 P below 65504.  With block 0's max as the

@@ -81,6 +81,14 @@ hipError_t launch_proj_tiled(const FwdParams& p, hipStream_t st);
 // 16-bit I/O (needs chunked slots).
 bool fused_w16_supported(int M, int C, int heads, int io);
 hipError_t launch_fused_w16(const FwdParams& p, hipStream_t st);
+// QKV projection + attention in one kernel for window sides 16 and 24, C = 32
+// x heads up to 1024, 16-bit I/O, x below 2 GiB (needs chunked slots); O goes
+// to buf.o in window-slot order for the projection GEMM.  flags: one int per
+// (window, head, wave) -- fused_qkv_attn_flag_count -- written by the main
+// launch (!redo); the redo launch recomputes the flagged items exactly.
+bool fused_qkv_attn_supported(int64_t tokens, int M, int C, int heads, int io);
+int64_t fused_qkv_attn_flag_count(int M, int64_t items);
+hipError_t launch_fused_qkv_attn(const FwdParams& p, int* flags, bool redo, hipStream_t st);
 // Attention for window side 7 with 16-bit I/O between the GEMMs (row-major
 // slots).
 bool w8_attn_supported(int M, int io);

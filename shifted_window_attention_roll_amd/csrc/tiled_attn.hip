@@ -128,8 +128,9 @@ void tiled_attn_kernel(FwdParams p, int n_items) {
       }
     };
 
-    // Unmasked windows take the fast path; masked ones, and the rare item
-    // whose logits outgrow the fast path's reference, the exact lazy one
+    // Unmasked windows take the fast path, and so do masked ones with the
+    // zero reference (cosine attention, bfloat16 P); the rest, and the rare
+    // item whose logits outgrow the fixed reference, the exact lazy one
     // (running the hook twice stages the same chunks twice).
     float o[QTL][8];
     bool done = false;
@@ -137,8 +138,12 @@ void tiled_attn_kernel(FwdParams p, int n_items) {
       done = attn_tiles<QT, VT, M, QTL, false, KvLayout::kSwizzled, TableMode::kTable1,
                         ZREF ? RefMode::kZero : RefMode::kBlock0>(
           qf, tile, ks[buf], vs[buf], rt, ninf, lane, M - g.s, false, false, o, hook);
+    else if constexpr (ZREF)
+      done = attn_tiles<QT, VT, M, QTL, true, KvLayout::kSwizzled, TableMode::kTable1,
+                        RefMode::kZero>(qf, tile, ks[buf], vs[buf], rt, ninf, lane, M - g.s, my,
+                                        mx, o, hook);
     if (!done)
-      attn_tiles<QT, VT, M, QTL, true, KvLayout::kSwizzled, TableMode::kTable1>(
+      attn_tiles<QT, VT, M, QTL, true, KvLayout::kSwizzled, TableMode::kTable1, RefMode::kLazy>(
           qf, tile, ks[buf], vs[buf], rt, ninf, lane, M - g.s, my, mx, o, hook);
 
     // O rows in slot order, columns h*32 + d: the lane's 8 dims, one store.

@@ -56,13 +56,17 @@ def test_workspace_size(lib):
     assert swin.workspace_size(_desc()) == 0
     # window 16 with <= 4 heads and 16-bit I/O is fused too
     assert swin.workspace_size(_desc(H=64, W=64, C=128, heads=4, M=16, s=8)) == 0
-    d = _desc(H=64, W=64, C=160, heads=5, M=16, s=8)
+    d = _desc(H=64, W=64, C=160, heads=5, M=8, s=4)
     T = 2 * 64 * 64
     assert swin.workspace_size(d) >= 4 * T * 160 * 2
+    # QKV fused into the attention (window 16 or 24): only O (and the redo
+    # flags) go through it
+    d64 = _desc(H=64, W=64, C=192, heads=6, M=16, s=8)
+    assert T * 192 * 2 <= swin.workspace_size(d64) < 2 * T * 192 * 2
     assert swin.workspace_size(_desc(B=0)) == 0
     assert swin.workspace_size(_desc(H=50)) == 0          # invalid -> 0
     # V2 with bf16 keeps q and k in float16: same byte count as bf16
-    assert swin.workspace_size(swin.make_desc(2, 64, 64, 160, 5, 16, 8, "v2", torch.bfloat16)) == \
+    assert swin.workspace_size(swin.make_desc(2, 64, 64, 160, 5, 8, 4, "v2", torch.bfloat16)) == \
         swin.workspace_size(d)
     d32 = swin.make_desc(2, 64, 64, 128, 4, 16, 8, "v1", torch.float32)
     assert swin.workspace_size(d32) >= 4 * T * 128 * 4
@@ -145,9 +149,24 @@ def test_kernel_names_and_timed_rejects(lib):
     tiled = ["qkv_tiled_kernel", "tiled_attn_kernel", "proj_tiled_kernel"]
     three = ["qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"]
     assert swin.kernel_names(d) == ["fused_w16_kernel"]
-    assert swin.kernel_names(_desc(H=64, W=64, C=160, heads=5, M=16, s=8)) == [
+    assert swin.kernel_names(_desc(H=64, W=64, C=160, heads=5, M=8, s=4)) == [
         "qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"]
+    assert swin.kernel_names(_desc(H=64, W=64, C=160, heads=5, M=16, s=8)) == [
+        "fused_qkv_attn_kernel", "fused_qkv_attn_redo_kernel", "proj_gemm_kernel"]
     assert swin.kernel_names(_desc(H=48, W=48, M=24, s=12, C=512, heads=16,
+                                   dtype=torch.bfloat16)) == ["fused_qkv_attn_kernel",
+                                                              "fused_qkv_attn_redo_kernel",
+                                                              "proj_tiled_kernel"]
+    assert swin.kernel_names(_desc(H=64, W=64, M=16, s=8, C=192, heads=6)) == [
+        "fused_qkv_attn_kernel", "fused_qkv_attn_redo_kernel", "proj_gemm_kernel"]
+    assert swin.kernel_names(_desc(H=48, W=48, M=24, s=12, C=96, heads=3,
+                                   dtype=torch.bfloat16)) == ["fused_qkv_attn_kernel",
+                                                              "fused_qkv_attn_redo_kernel",
+                                                              "proj_gemm_kernel"]
+    # x of 2 GiB or more: the three-kernel plan
+    assert swin.kernel_names(_desc(B=232, H=96, W=96, M=24, s=12, C=512, heads=16,
+                                   dtype=torch.bfloat16))[0] == "qkv_gemm_kernel"
+    assert swin.kernel_names(_desc(H=48, W=48, M=8, s=4, C=512, heads=16,
                                    dtype=torch.bfloat16)) == tiled
     assert swin.kernel_names(_desc(H=64, W=64, M=16, s=8, C=128, heads=4,
                                    dtype=torch.float32)) == three
@@ -343,6 +362,7 @@ def test_sparse24_rejects_before_launch(lib):
 # Kernels the forward can enqueue, per plan: the parity cases with the tau clip
 # and the descriptor overrides (test_gpu_parity.PLAN_CASES) must reach each.
 PLAN_KERNELS = {"fused_w8_kernel", "fused_window_kernel", "fused_w16_kernel",
+                "fused_qkv_attn_kernel", "fused_qkv_attn_redo_kernel",
                 "tiled_attn_kernel", "w8_attn_kernel", "window_attn_kernel",
                 "qkv_tiled_kernel", "qkv_gemm_kernel", "proj_tiled_kernel", "proj_gemm_kernel"}
 
