@@ -75,8 +75,9 @@ def stage_work(case):
         "fused_w8_kernel": ((8 * C * C + 4 * N * C) * T, T * 2 * C * e + 4 * C * C * e + tab),
         # QKV projection + attention: x in, O out, the QKV weights and the table
         "fused_qkv_attn_kernel": ((6 * C * C + 4 * N * C) * T, T * 2 * C * e + 3 * C * C * e + tab),
-        # the exact pass over flagged items (none on the workloads): flags only
+        # the exact passes over flagged items (none on the workloads): flags only
         "fused_qkv_attn_redo_kernel": (0, 1),
+        "fused_w16_redo_kernel": (0, 1),
         "qkv_gemm_kernel": (6 * C * C * T, T * (C * e + 2 * C * eqk + C * e) + 3 * C * C * e),
         "qkv_tiled_kernel": (6 * C * C * T, T * (C * e + 2 * C * eqk + C * e) + 3 * C * C * e),
         "proj_tiled_kernel": (2 * C * C * T, T * 2 * C * e + C * C * e),
@@ -198,7 +199,8 @@ class Runner:
 # taken on a kernel stay valid while only other kernels change.
 KERNEL_SOURCE = {
     "fused_window_kernel": "fused_window.hip", "fused_w8_kernel": "fused_w8.hip",
-    "fused_w16_kernel": "fused_w16.hip", "tiled_attn_kernel": "tiled_attn.hip",
+    "fused_w16_kernel": "fused_w16.hip", "fused_w16_redo_kernel": "fused_w16.hip",
+    "tiled_attn_kernel": "tiled_attn.hip",
     "fused_qkv_attn_kernel": "fused_qkv_attn.hip", "fused_qkv_attn_redo_kernel": "fused_qkv_attn.hip",
     "window_attn_kernel": "window_attn.hip", "w8_attn_kernel": "w8_attn.hip",
     "qkv_tiled_kernel": "gemm_tiled.hip",

@@ -84,7 +84,8 @@ Plan choose_plan(const swin_wmsa_desc* d) {
   const int heads = d->heads;
   if (fused_w8_supported(d->M, d->C, heads, io_type(d))) return kPlanFusedW8;
   if (d->M * d->M <= 64 && heads <= 4 && d->C == kHeadDim * heads) return kPlanFusedSmall;
-  if (fused_w16_supported(d->M, d->C, heads, io_type(d))) return kPlanFusedW16;
+  if (fused_w16_supported((int64_t)d->B * d->H * d->W, d->M, d->C, heads, io_type(d)))
+    return kPlanFusedW16;
   if (fused_qkv_attn_supported((int64_t)d->B * d->H * d->W, d->M, d->C, heads, io_type(d)))
     return kPlanFusedQkv;
   if (tiled_attn_supported(d->M, io_type(d))) return kPlanTiled;
@@ -102,8 +103,12 @@ struct WsLayout {
 
 WsLayout ws_layout(const swin_wmsa_desc* d) {
   const Plan plan = choose_plan(d);
-  if (plan == kPlanFusedSmall || plan == kPlanFusedW16 || plan == kPlanFusedW8)
-    return WsLayout{0, 0, 0, 0, 0};
+  if (plan == kPlanFusedSmall || plan == kPlanFusedW8) return WsLayout{0, 0, 0, 0, 0};
+  if (plan == kPlanFusedW16) {  // the redo flags only (at offset 0)
+    const size_t windows = (size_t)d->B * (d->H / d->M) * (d->W / d->M);
+    return WsLayout{0, 0, 0, 0,
+                    round_up((size_t)fused_w16_flag_count(d->heads, windows) * 4, 256)};
+  }
   const size_t tokens = (size_t)d->B * d->H * d->W;
   const size_t e = elem_bytes(d->dtype);
   const size_t eq = qk_type(d) == kF32 ? 4 : 2;
@@ -206,12 +211,12 @@ size_t swin_wmsa_workspace_size(const swin_wmsa_desc* d) {
   return ws_layout(d).total;
 }
 
-static const int kPlanCount[6] = {1, 3, 3, 1, 1, 3};
+static const int kPlanCount[6] = {1, 3, 3, 2, 1, 3};
 
 static const char* stage_name(const swin_wmsa_desc* d, int i) {
   const Plan plan = choose_plan(d);
   if (plan == kPlanFusedSmall) return "fused_window_kernel";
-  if (plan == kPlanFusedW16) return "fused_w16_kernel";
+  if (plan == kPlanFusedW16) return i == 0 ? "fused_w16_kernel" : "fused_w16_redo_kernel";
   if (plan == kPlanFusedW8) return "fused_w8_kernel";
   const bool tg = use_tiled_gemm(d);
   if (plan == kPlanFusedQkv)
@@ -304,12 +309,18 @@ static swin_status wmsa_forward(const swin_wmsa_desc* d, const void* x, const vo
     return events ? hipEventRecord(static_cast<hipEvent_t>(events[i]), hs) : hipSuccess;
   };
   hipError_t err = mark(0);
-  if (plan == kPlanFusedSmall || plan == kPlanFusedW16 || plan == kPlanFusedW8) {
+  if (plan == kPlanFusedSmall || plan == kPlanFusedW8) {
     if (err == hipSuccess)
-      err = plan == kPlanFusedSmall ? launch_fused_window(p, hs)
-            : plan == kPlanFusedW16 ? launch_fused_w16(p, hs)
-                                    : launch_fused_w8(p, hs);
+      err = plan == kPlanFusedSmall ? launch_fused_window(p, hs) : launch_fused_w8(p, hs);
     if (err == hipSuccess) err = mark(1);
+    return from_hip(err);
+  }
+  if (plan == kPlanFusedW16) {
+    int* flags = reinterpret_cast<int*>(ws);
+    if (err == hipSuccess) err = launch_fused_w16(p, flags, false, hs);
+    if (err == hipSuccess) err = mark(1);
+    if (err == hipSuccess) err = launch_fused_w16(p, flags, true, hs);
+    if (err == hipSuccess) err = mark(2);
     return from_hip(err);
   }
   const bool tg = use_tiled_gemm(d);

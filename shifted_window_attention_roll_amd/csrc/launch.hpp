@@ -78,9 +78,12 @@ bool tiled_gemm_supported(int C, int io);
 hipError_t launch_qkv_tiled(const FwdParams& p, hipStream_t st);
 hipError_t launch_proj_tiled(const FwdParams& p, hipStream_t st);
 // Single-kernel forward for window side 16 with C = 32 * heads, heads <= 4,
-// 16-bit I/O (needs chunked slots).
-bool fused_w16_supported(int M, int C, int heads, int io);
-hipError_t launch_fused_w16(const FwdParams& p, hipStream_t st);
+// 16-bit I/O, x below 2^31 elements (needs chunked slots).  flags: one int per
+// (window, wave) -- fused_w16_flag_count -- written by the main launch
+// (!redo); the redo launch recomputes the flagged windows exactly.
+bool fused_w16_supported(int64_t tokens, int M, int C, int heads, int io);
+int64_t fused_w16_flag_count(int heads, int64_t windows);
+hipError_t launch_fused_w16(const FwdParams& p, int* flags, bool redo, hipStream_t st);
 // QKV projection + attention in one kernel for window sides 16 and 24, C = 32
 // x heads up to 1024, 16-bit I/O, x below 2 GiB (needs chunked slots); O goes
 // to buf.o in window-slot order for the projection GEMM.  flags: one int per

@@ -54,8 +54,9 @@ def _desc(**kw):
 def test_workspace_size(lib):
     # small windows with <= 4 heads run as one fused kernel: no workspace
     assert swin.workspace_size(_desc()) == 0
-    # window 16 with <= 4 heads and 16-bit I/O is fused too
-    assert swin.workspace_size(_desc(H=64, W=64, C=128, heads=4, M=16, s=8)) == 0
+    # window 16 with <= 4 heads and 16-bit I/O is fused too: one redo flag per
+    # wave (2 per head) and window
+    assert swin.workspace_size(_desc(H=64, W=64, C=128, heads=4, M=16, s=8)) == 2 * 16 * 8 * 4
     d = _desc(H=64, W=64, C=160, heads=5, M=8, s=4)
     T = 2 * 64 * 64
     assert swin.workspace_size(d) >= 4 * T * 160 * 2
@@ -148,7 +149,7 @@ def test_kernel_names_and_timed_rejects(lib):
     d = _desc(H=64, W=64, C=128, heads=4, M=16, s=8)
     tiled = ["qkv_tiled_kernel", "tiled_attn_kernel", "proj_tiled_kernel"]
     three = ["qkv_gemm_kernel", "window_attn_kernel", "proj_gemm_kernel"]
-    assert swin.kernel_names(d) == ["fused_w16_kernel"]
+    assert swin.kernel_names(d) == ["fused_w16_kernel", "fused_w16_redo_kernel"]
     assert swin.kernel_names(_desc(H=64, W=64, C=160, heads=5, M=8, s=4)) == [
         "qkv_gemm_kernel", "tiled_attn_kernel", "proj_gemm_kernel"]
     assert swin.kernel_names(_desc(H=64, W=64, C=160, heads=5, M=16, s=8)) == [
@@ -163,6 +164,9 @@ def test_kernel_names_and_timed_rejects(lib):
                                    dtype=torch.bfloat16)) == ["fused_qkv_attn_kernel",
                                                               "fused_qkv_attn_redo_kernel",
                                                               "proj_gemm_kernel"]
+    # window 16 with x of 2^31 elements or more: not the single fused kernel
+    assert swin.kernel_names(_desc(B=4096, H=64, W=64, C=128, heads=4, M=16, s=8,
+                                   dtype=torch.bfloat16))[0] != "fused_w16_kernel"
     # x of 2 GiB or more: the three-kernel plan
     assert swin.kernel_names(_desc(B=232, H=96, W=96, M=24, s=12, C=512, heads=16,
                                    dtype=torch.bfloat16))[0] == "qkv_gemm_kernel"
@@ -186,7 +190,8 @@ def test_kernel_names_and_timed_rejects(lib):
     assert swin.kernel_names(_desc(H=48, W=48, M=12, s=6, C=128, heads=4)) == three
     assert swin.kernel_names(_desc(H=48, W=48, M=12, s=6, C=256, heads=8)) == [
         "qkv_tiled_kernel", "window_attn_kernel", "proj_tiled_kernel"]
-    assert swin.kernel_names(_desc(H=48, W=48, M=16, s=6, C=96, heads=3)) == ["fused_w16_kernel"]
+    assert swin.kernel_names(_desc(H=48, W=48, M=16, s=6, C=96, heads=3)) == [
+        "fused_w16_kernel", "fused_w16_redo_kernel"]
     assert lib.swin_wmsa_kernel_count(ctypes.byref(_desc(H=50))) == 0
     assert lib.swin_wmsa_kernel_name(ctypes.byref(d), 3) is None
     small = _desc(B=1, H=16, W=16, C=160, heads=5, M=16, s=3)  # needs a workspace
@@ -361,7 +366,7 @@ def test_sparse24_rejects_before_launch(lib):
 
 # Kernels the forward can enqueue, per plan: the parity cases with the tau clip
 # and the descriptor overrides (test_gpu_parity.PLAN_CASES) must reach each.
-PLAN_KERNELS = {"fused_w8_kernel", "fused_window_kernel", "fused_w16_kernel",
+PLAN_KERNELS = {"fused_w8_kernel", "fused_window_kernel", "fused_w16_kernel", "fused_w16_redo_kernel",
                 "fused_qkv_attn_kernel", "fused_qkv_attn_redo_kernel",
                 "tiled_attn_kernel", "w8_attn_kernel", "window_attn_kernel",
                 "qkv_tiled_kernel", "qkv_gemm_kernel", "proj_tiled_kernel", "proj_gemm_kernel"}
