@@ -97,34 +97,6 @@ __device__ __forceinline__ vec8<T> cvt8(const float (&v)[8], float mult) {
   return o;
 }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource (32-bit byte bound) as four scalar dwords.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
-}
-
-// LDS byte address of a __shared__ object.
-template <typename P>
-__device__ __forceinline__ uint32_t lds_addr(P* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)p);
-}
-
-// One 16-byte direct-to-LDS load per lane: lane L's bytes voff + soff of the
-// buffer land at LDS byte lds + 16 L.  Written as inline assembly so that the
-// compiler does not see the LDS write: it would otherwise wait for every such
-// load before any later LDS read, including the loads meant to fly two steps
-// ahead; the waits are explicit instead (wait_vm, then a barrier).  There is
-// no output register.
-__device__ __forceinline__ void lds_dma16(const i32x4& rs, uint32_t lds, uint32_t voff,
-                                          uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds), "v"(voff), "s"(rs), "s"(soff)
-               : "memory", "m0");
-}
-
 // The kernel body.  !REDO: every (window, head) item of the launch; a wave
 // whose fixed-reference row sums leave the safe range (attn_core.hpp) sets
 // flags[(win * heads + h) * WAVES + wave] = 1 (else 0) and leaves its O to the

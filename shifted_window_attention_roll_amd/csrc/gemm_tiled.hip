@@ -107,13 +107,27 @@ __device__ __forceinline__ TileWalk tile_walk(int ntiles) {
   return t;
 }
 
+// Tile count of the XCD's first workgroup (the largest).
+__device__ __forceinline__ int tile_walk_first_count(int ntiles) {
+  const int G = gridDim.x, id = blockIdx.x;
+  const int nx = G < 8 ? G : 8;
+  const int x = id % nx;
+  const int wpx = (G - x + nx - 1) / nx;
+  const int cnt = ntiles / nx + (x < ntiles % nx ? 1 : 0);
+  return (cnt + wpx - 1) / wpx;
+}
+
 // The persistent main loop.  src(tile, TileSrc&) fills the source offsets of a
-// tile, epi(tile, acc) consumes its accumulators.  acc[i][j] covers token tile
+// tile, epi(tile, acc) consumes its accumulators.  With EPI_VM > 0, epi returns
+// the number of vector-memory instructions it issued (stores only); when that
+// is exactly EPI_VM, the next tile's first wait lets them stay in flight (they
+// were issued after the loads it waits for), so the stores drain while stage 0
+// is multiplied instead of stalling every workgroup at once.  acc[i][j] covers token tile
 // i x channel tile j in C^T form; the weight rows of each pair of channel
 // tiles are interleaved so that lane l holds token 16i + l%16 and channels
 // 32(j/2) + 8(l/16) + 4(j%2) + r: 8 consecutive channels, one 16-byte store.
-template <typename T, int BM, int BN, int WGM, int WGN, int NK, bool LINEAR, class SrcFn,
-          class EpiFn>
+template <typename T, int BM, int BN, int WGM, int WGN, int NK, bool LINEAR, int EPI_VM = 0,
+          class SrcFn, class EpiFn>
 __device__ __forceinline__ void run_tiles(const char* __restrict__ A, uint32_t a_bytes,
                                           const char* __restrict__ Bw, uint32_t b_bytes,
                                           uint32_t rowbytes, char* smem, int ntiles, SrcFn src,
@@ -121,38 +135,45 @@ __device__ __forceinline__ void run_tiles(const char* __restrict__ A, uint32_t a
   using G = Cfg<BM, BN, WGM, WGN>;
   using Src = TileSrc<G::A_INS, LINEAR>;
   static_assert(NK % 2 == 0 && NK >= kPrefetch, "stage parity and touch distance");
+  static_assert(EPI_VM >= 0 && EPI_VM + 1 <= 63, "vmcnt range");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WGN, wn = wave - (wave / WGN) * WGN;
   const TileWalk tw = tile_walk(ntiles);
   if (tw.count <= 0) return;
-  char* sink = smem + 2 * G::STAGE + wave * 256;
+  if constexpr (EPI_VM > 0) {
+    // Workgroups with one tile fewer than the first of their XCD start about
+    // half a tile later (NK stages at about 2048 cycles each, halved; they
+    // would wait at the end anyway): their epilogue stores then go out while
+    // the others multiply, instead of every workgroup storing at once.
+    if (tw.count < tile_walk_first_count(ntiles))
+      for (int i = 0; i < NK / 2; ++i) __builtin_amdgcn_s_sleep(64);
+  }
 
   // Buffer resources (raw, bounds = the whole tensor): the lane offset is a
   // 32-bit VGPR, the stage offset a scalar, so a load costs no vector ALU.
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(A), (short)0, (int)a_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rbw =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(Bw), (short)0, (int)b_bytes, 0x00020000);
+  // The loads are issued as inline assembly (common.hpp): the compiler, which
+  // would see an LDS write, otherwise waits for each stage's loads right after
+  // issuing them (before the next fragment reads), and the pipeline is gone.
+  // Every wait is explicit (wait_vm, then a barrier).
+  const i32x4 ra = make_rsrc(A, a_bytes);
+  const i32x4 rbw = make_rsrc(Bw, b_bytes);
+  const uint32_t smem_a = lds_addr(smem);
   auto dma = [&](const Src& sr, int buf, int k) {
-    char* sa = smem + buf * G::STAGE;
-    char* sb = sa + G::A_BYTES;
+    const uint32_t sa = smem_a + buf * G::STAGE;
+    const uint32_t sb = sa + G::A_BYTES;
 #pragma unroll
     for (int i = 0; i < G::A_INS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_vptr)(sa + (wave * G::A_INS + i) * 1024), 16, sr.a[LINEAR ? 0 : i],
-          k * (kStageK * 2) + (LINEAR ? i * 8 * rowbytes : 0), 0, 0);
+      lds_dma16(ra, sa + (wave * G::A_INS + i) * 1024, sr.a[LINEAR ? 0 : i],
+                k * (kStageK * 2) + (LINEAR ? i * 8 * rowbytes : 0));
 #pragma unroll
     for (int i = 0; i < G::B_INS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbw, (lds_vptr)(sb + (wave * G::B_INS + i) * 1024),
-                                               16, sr.b, k * (kStageK * 2) + i * 8 * rowbytes, 0,
-                                               0);
+      lds_dma16(rbw, sb + (wave * G::B_INS + i) * 1024, sr.b, k * (kStageK * 2) + i * 8 * rowbytes);
   };
   // One 4-byte load per A row of stage k: the line lands in L2 (and a
   // throw-away LDS sink); nothing reads it.
   auto touch = [&](const Src& sr, int k) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)sink, 4, sr.touch, k * (kStageK * 2),
-                                             0, 0);
+    lds_dma4(ra, smem_a + 2 * G::STAGE + wave * 256, sr.touch, k * (kStageK * 2));
   };
 
   // Fragment lane offsets inside a 32-row pair of tiles: row (t = tile parity)
@@ -209,6 +230,7 @@ __device__ __forceinline__ void run_tiles(const char* __restrict__ A, uint32_t a
   dma(cur, 1, 1);
   touch(cur, 3);
 
+  int issued = -1;  // vector-memory instructions of the previous epilogue
   for (int it = 0; it < tw.count; ++it) {
     const bool more = it + 1 < tw.count;
 #pragma unroll
@@ -220,7 +242,12 @@ __device__ __forceinline__ void run_tiles(const char* __restrict__ A, uint32_t a
       __builtin_amdgcn_sched_barrier(0);
       multiply(af0, bf0);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<1>();  // this wave's loads of stage k+1 have landed
+      // This wave's loads of stage k+1 have landed (at k = 0 they are followed
+      // by the touch and, possibly, the previous epilogue's EPI_VM stores).
+      if (EPI_VM > 0 && k == 0 && issued == EPI_VM)
+        wait_vm<1 + EPI_VM>();
+      else
+        wait_vm<1>();
       __syncthreads();  // ... everyone's; and buffer k%2 is free
       // Loads of stage k+2 (this tile or the next), touch of stage k+4.
       if (k + 2 < NK) dma(cur, k & 1, k + 2);
@@ -233,7 +260,10 @@ __device__ __forceinline__ void run_tiles(const char* __restrict__ A, uint32_t a
       __builtin_amdgcn_sched_barrier(0);
       if (k + 1 < NK) read_frags((k + 1) & 1, 1, af1, bf1);
     }
-    epi(tile, acc);
+    if constexpr (EPI_VM > 0)
+      issued = epi(tile, acc);
+    else
+      epi(tile, acc);
     // The next tile's stage 0 (buffer 0) was published by the last barrier;
     // its fragments are read after the epilogue so that they do not occupy
     // registers during it (stale and unused after the last tile).
@@ -369,7 +399,9 @@ template <typename T, int BM, int BN, int WGM, int WGN, int NK>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_tiled_kernel(FwdParams p) {
   using G = Cfg<BM, BN, WGM, WGN>;
   using Src = TileSrc<G::A_INS, true>;
+  constexpr int kMaxC = 512;  // tiled_gemm_supported
   __shared__ __attribute__((aligned(1024))) char smem[G::SMEM];
+  __shared__ float bsm[kMaxC];  // the projection bias
   const Geom& g = p.g;
   const int rows = g.B * g.H * g.W;
   const int C = g.C;
@@ -391,7 +423,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_tiled_kernel(FwdParams
   };
   const T* bp = static_cast<const T*>(p.b_proj);
   T* y = static_cast<T*>(p.y);
-  auto epi = [&](int tile, f32x4 (&acc)[G::TM][G::TN]) {
+  // Published by the first barrier of run_tiles.
+  for (int i = threadIdx.x; i < C; i += G::THREADS) bsm[i] = bp ? (float)bp[i] : 0.f;
+  constexpr int kStores = G::TM * (G::TN / 2);  // a full tile's stores per lane
+  auto epi = [&](int tile, f32x4 (&acc)[G::TM][G::TN]) -> int {
     const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
     const int m0 = rb * BM, n0 = cbk * BN;
     int rbase = m0 + wm * G::WM + i16;
@@ -407,14 +442,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_tiled_kernel(FwdParams
       const int row = rbase + 16 * i;
       dst[i] = row < rows ? (uint32_t)src_token(g, row) * (uint32_t)C : 0xffffffffu;
     }
-    // All loads before the first store (in-order memory counter).
     float b[G::TN / 2][8];
 #pragma unroll
-    for (int jh = 0; jh < G::TN / 2; ++jh) load_bias8(bp, c00 + 32 * jh, b[jh]);
-    // lane: token 16i + i16; channels 32jh + 8 g4 + e.
+    for (int jh = 0; jh < G::TN / 2; ++jh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[jh][e] = bsm[c00 + 32 * jh + e];
+    // lane: token 16i + i16; channels 32jh + 8 g4 + e.  No loads from global
+    // memory here: the stores are the only vector-memory instructions.
+    int n = 0;
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
       if (dst[i] == 0xffffffffu) continue;
+      n += G::TN / 2;
 #pragma unroll
       for (int jh = 0; jh < G::TN / 2; ++jh) {
         float v[8];
@@ -426,8 +465,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void proj_tiled_kernel(FwdParams
         store8(y + dst[i] + c00 + 32 * jh, v, 1.0f);
       }
     }
+    // Per-lane count; EPI_VM needs the wave's count: rows past the end skip
+    // stores in some lanes only, so a tile with any such row reports -1.
+    return __builtin_amdgcn_readfirstlane(n) == kStores && __all(n == kStores) ? kStores : -1;
   };
-  run_tiles<T, BM, BN, WGM, WGN, NK, true>(static_cast<const char*>(p.buf.o),
+  run_tiles<T, BM, BN, WGM, WGN, NK, true, kStores>(static_cast<const char*>(p.buf.o),
                                            (uint32_t)rows * rowbytes,
                                            static_cast<const char*>(p.w_proj), C * rowbytes,
                                            rowbytes, smem, ntiles, src, epi);
