@@ -121,6 +121,7 @@ __device__ __forceinline__ void fqa_body(const FwdParams& p, int* flags) {
   __shared__ __attribute__((aligned(16))) float rt[TSZ];
   __shared__ __attribute__((aligned(16))) float ninf[8];
   __shared__ float red[WAVES];
+  __shared__ __attribute__((aligned(16))) float bqs[96];  // the head's q, k, v biases
   QT* ks = reinterpret_cast<QT*>(kvx);  // swizzled rows (kv_frag.hpp)
   T* vs = reinterpret_cast<T*>(kvx + N * D * 2);
 
@@ -254,6 +255,8 @@ __device__ __forceinline__ void fqa_body(const FwdParams& p, int* flags) {
       // Every wave is past its last read of the previous head's table.
       __syncthreads();
       fill_bias_table<M>(rt, p.table, heads, h, tid, NT);
+      for (int e = tid; e < 96; e += NT)
+        bqs[e] = bq ? (float)bq[(e >> 5) * C + h * D + (e & 31)] : 0.f;
       if constexpr (ZREF) {
         // |q . k| <= log2(e) / max(tau, tau_min) (q carries that factor, both
         // are unit vectors; 2^-8 covers their float16 rounding), so no logit
@@ -342,7 +345,7 @@ __device__ __forceinline__ void fqa_body(const FwdParams& p, int* flags) {
 #pragma unroll
     for (int pt = 0; pt < 3; ++pt)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) bias[pt][e] = bq ? (float)bq[pt * C + h * D + 8 * g4 + e] : 0.f;
+      for (int e = 0; e < 8; ++e) bias[pt][e] = bqs[32 * pt + 8 * g4 + e];
     vec8<QT> qf[QTL];
 #pragma unroll
     for (int j = 0; j < QTL; ++j) {
