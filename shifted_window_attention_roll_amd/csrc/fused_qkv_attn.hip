@@ -50,13 +50,21 @@ struct FqaCfg<24> {
 };
 
 // One phase-1 step: 32 channels, i.e. 64-byte rows of four 16-byte chunks.
-// Token rows: chunk q of slot row r sits at position q ^ ((r / 4) % 4), so the
-// 16 consecutive rows a fragment read touches cover 256 distinct bytes modulo
-// 256 (every bank once per 16 lanes).  Weight rows: chunk q of row r at q ^
-// ((r / 8) % 4); the 16 rows a fragment read touches are 8a + b + 4t (a, b in
-// 0..3), distinct in (r % 4, r / 8 % 4).
-__device__ __forceinline__ int xsw(int r, int q) { return r * 32 + ((q ^ ((r >> 2) & 3)) << 3); }
-__device__ __forceinline__ int wsw(int r, int q) { return r * 32 + ((q ^ ((r >> 3) & 3)) << 3); }
+// Chunk q of LDS row r sits at position q ^ sw(r), sw(r) = (r/2 ^ r/4 ^ r/16)
+// % 4: for the 16 consecutive rows of a fragment read, any 8, 16 or 32
+// consecutive lanes then touch distinct 16-byte bank slots modulo 128, 256 and
+// 512 bytes.  Weight rows are stored permuted inside each 32-row part (LDS
+// row 16t + 4a + b holds row 8a + 4t + b), so that the 16 rows 8a + 4t + b of
+// a fragment (a, b in 0..3) are 16 consecutive LDS rows too.
+__device__ __forceinline__ int sw(int r) { return ((r >> 1) ^ (r >> 2) ^ (r >> 4)) & 3; }
+__device__ __forceinline__ int xsw(int r, int q) { return r * 32 + ((q ^ sw(r)) << 3); }
+// Weight row r (part r / 32, interleaved fragment order) -> its LDS row, and back.
+__device__ __forceinline__ int wrow_lds(int r) {
+  return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
+}
+__device__ __forceinline__ int wrow_of_lds(int l) {
+  return (l & ~31) | (((l >> 2) & 3) << 3) | (((l >> 4) & 1) << 2) | (l & 3);
+}
 
 // s_waitcnt vmcnt(N) only: all but the last N vector-memory operations of this
 // wave have completed (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4]
@@ -201,11 +209,12 @@ __device__ __forceinline__ void fqa_body(const FwdParams& p, int* flags) {
     for (int u = 0; u < XU; ++u) {
       const int r = 16 * (wave + WAVES * u) + (lane >> 2);
       off[u] = slot_token(win, r) * (uint32_t)(C * (int)sizeof(T)) +
-               (uint32_t)((slot ^ ((r >> 2) & 3)) << 4);
+               (uint32_t)((slot ^ sw(r)) << 4);
     }
-    const int r = 16 * wave + (lane >> 2);  // weight row (wave < WI)
+    const int l = 16 * wave + (lane >> 2);  // LDS weight row (wave < WI)
+    const int r = wrow_of_lds(l);
     const uint32_t row = (uint32_t)((r >> 5) * C + h * D + (r & 31));
-    off[XU] = row * (uint32_t)(C * (int)sizeof(T)) + (uint32_t)((slot ^ ((r >> 3) & 3)) << 4);
+    off[XU] = row * (uint32_t)(C * (int)sizeof(T)) + (uint32_t)((slot ^ sw(l)) << 4);
   };
   // Step s of an item into buffer (s + 2) % 3: step 0 lands in the buffer
   // past K and V, so that it can be loaded during the previous item's
@@ -311,7 +320,7 @@ __device__ __forceinline__ void fqa_body(const FwdParams& p, int* flags) {
       for (int pt = 0; pt < 3; ++pt)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          wf[pt][t] = *reinterpret_cast<const vec8<T>*>(&wb[wsw(32 * pt + prow0 + 4 * t, g4)]);
+          wf[pt][t] = *reinterpret_cast<const vec8<T>*>(&wb[xsw(wrow_lds(32 * pt + prow0 + 4 * t), g4)]);
       // Every fragment read of the step goes out before its products.
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
