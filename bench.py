@@ -621,6 +621,20 @@ def _stats_rows(d):
     return rows
 
 
+def _launch_durations(d):
+    """Per-launch durations (us) by kernel name, in dispatch order, from the
+    kernel_trace.csv files under d."""
+    import csv
+    import collections
+    out = collections.defaultdict(list)
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(f) as fh:
+            rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+        for r in rows:
+            out[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return out
+
+
 def trace_summarize(name, trace_dir, command):
     """rocprofv3 --kernel-trace --stats output -> profiles/kernel_trace_<workload>.md:
     per kernel of the forward, calls, average / min / max duration and the
@@ -635,10 +649,14 @@ def trace_summarize(name, trace_dir, command):
     peak_f = PEAK_TFLOPS[case.dtype]
     lines = [f"# Kernel trace, {name}", "", f"Command: `{command}`", "",
              "Durations from rocprofv3 `--kernel-trace --stats` (every launch of the run, "
-             "warm-up included).  Rate = the kernel's algorithmic flops (bytes) per launch / "
-             "its average duration.", "",
-             "| kernel | calls | avg us | min us | max us | algorithmic GFLOP | TFLOP/s | "
-             "frac of MFMA peak | algorithmic MB | GB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+             "warm-up included); `avg after 5` and `median` from the per-launch trace of the "
+             "same run, without each kernel's first 5 launches (the bench's warm-up), for "
+             "comparison with the bench's event-timed launches.  Rate = the kernel's "
+             "algorithmic flops (bytes) per launch / its average duration.", "",
+             "| kernel | calls | avg us | min us | max us | avg after 5 us | median us | "
+             "algorithmic GFLOP | TFLOP/s | frac of MFMA peak | algorithmic MB | GB/s |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    launches = _launch_durations(trace_dir)
     total = 0.0
     for r in _stats_rows(trace_dir):
         k = next((n for n in kernels if n in r["Name"]), None)
@@ -647,7 +665,9 @@ def trace_summarize(name, trace_dir, command):
         avg, mn, mx = float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3
         fl, by = work[k]
         total += avg
-        lines.append(f"| {k} | {r['Calls']} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {fl / 1e9:.2f} | "
+        ds = launches.get(r["Name"], [])[5:]
+        tail = f"{sum(ds) / len(ds):.1f} | {sorted(ds)[len(ds) // 2]:.1f}" if ds else "- | -"
+        lines.append(f"| {k} | {r['Calls']} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {tail} | {fl / 1e9:.2f} | "
                      f"{fl / (avg * 1e-6) / 1e12:.0f} | {fl / (avg * 1e-6) / 1e12 / peak_f:.3f} | "
                      f"{by / 1e6:.1f} | {by / (avg * 1e-6) / 1e9:.0f} |")
     T = case.tokens * len(case.blocks)
