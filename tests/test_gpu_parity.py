@@ -99,7 +99,7 @@ SMALL = [
     (2, 48, 24, 96, 3, 24, 7, "fp16", "v2", 0.1),    # split 17: inside chunk 2
     (1, 16, 16, 32, 1, 16, 8, "bf16", "v1", 0.3),    # window = image, shifted
     (1, 24, 48, 160, 5, 8, 0, "bf16", "v2", 0.1),    # no shift
-    (1, 32, 32, 160, 5, 16, 8, "bf16", "v2", 0.1),   # window 16, 5 heads: three kernels
+    (1, 32, 32, 160, 5, 16, 8, "bf16", "v2", 0.1),   # window 16, 5 heads: QKV fused into the attention
     (2, 32, 48, 96, 3, 16, 11, "fp16", "v1", 0.1),   # fused window 16: split 5 in chunk 0
     # fused window 7 / 8 (8 x 8 slot grid): heads 1 - 4, both modes, splits 1 .. 7
     (1, 14, 14, 32, 1, 7, 3, "fp16", "v2", 0.1),
@@ -137,8 +137,8 @@ def test_wmsa_small(gpu, B, H, W, C, heads, M, s, dtype, mode, bias_std):
     (1, 32, 32, 128, 4, 16, 8, "fp16", 6.0),    # fused window 16
     (1, 32, 32, 128, 4, 16, 0, "bf16", 40.0),   # fused window 16, every window unmasked
     (1, 16, 24, 256, 8, 8, 4, "bf16", 80.0),    # tiled, window 8
-    (1, 32, 32, 160, 5, 16, 8, "fp16", 6.0),    # tiled, window 16
-    (1, 48, 48, 96, 3, 24, 12, "bf16", 40.0),   # tiled, window 24
+    (1, 32, 32, 160, 5, 16, 8, "fp16", 6.0),    # QKV fused into the attention, window 16
+    (1, 48, 48, 96, 3, 24, 12, "bf16", 40.0),   # QKV fused into the attention, window 24
     (2, 14, 14, 96, 3, 7, 3, "fp16", 6.0),      # fused window 7
     (1, 16, 16, 64, 2, 8, 4, "bf16", 80.0),     # fused window 8
     (1, 14, 21, 192, 6, 7, 3, "bf16", 80.0),    # window 7 between the GEMMs
@@ -156,13 +156,13 @@ def test_wmsa_large_bias(gpu, B, H, W, C, heads, M, s, dtype, table_std):
 
 
 # Cosine attention with one relative-position entry raised far above the rest:
-# the shifted-table (zero) reference of the tiled kernel sees its other rows'
-# exponentials underflow and hands over to the exact lazy pass; the block-0
-# reference of the window-16 kernel sees the spike's row sums overflow.
+# the shifted-table (zero) reference of the attention core sees the other rows'
+# exponentials underflow, and the wave hands its item over to the exact lazy
+# pass (tiled attention, QKV fused into the attention, window-16 kernel).
 @pytest.mark.parametrize("B,H,W,C,heads,M,s", [
     (1, 24, 48, 160, 5, 8, 0),     # tiled, window 8, every window unmasked
-    (1, 32, 32, 160, 5, 16, 8),    # tiled, window 16
-    (1, 48, 48, 96, 3, 24, 12),    # tiled, window 24
+    (1, 32, 32, 160, 5, 16, 8),    # QKV fused into the attention, window 16
+    (1, 48, 48, 96, 3, 24, 12),    # QKV fused into the attention, window 24
     (1, 32, 32, 128, 4, 16, 0),    # fused window 16
 ])
 def test_wmsa_v2_table_spike(gpu, B, H, W, C, heads, M, s):
@@ -226,9 +226,9 @@ PLAN_CASES = [
     (1, 12, 12, 64, 2, 6, 3, "bf16"),     # fused small window
     (1, 10, 10, 64, 2, 5, 2, "fp32"),     # fused small window, float32
     (2, 32, 32, 128, 4, 16, 8, "bf16"),   # fused window 16
-    (1, 32, 32, 160, 5, 16, 8, "bf16"),   # tiled attention between the GEMMs, window 16
-    (1, 48, 48, 96, 3, 24, 12, "bf16"),   # tiled attention, window 24
-    (1, 48, 48, 512, 16, 24, 12, "bf16"),  # window 24 with C = 512 (tiled GEMMs)
+    (1, 32, 32, 160, 5, 16, 8, "bf16"),   # QKV fused into the attention, window 16
+    (1, 48, 48, 96, 3, 24, 12, "bf16"),   # QKV fused into the attention, window 24
+    (1, 48, 48, 512, 16, 24, 12, "bf16"),  # window 24 with C = 512 (tiled projection)
     (1, 16, 24, 256, 8, 8, 4, "fp16"),    # tiled attention, window 8, tiled GEMMs
     (1, 14, 21, 192, 6, 7, 3, "bf16"),    # window 7 between the GEMMs
     (1, 24, 24, 160, 5, 12, 6, "bf16"),   # general three kernels
