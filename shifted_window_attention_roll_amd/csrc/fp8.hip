@@ -331,6 +331,7 @@ hipError_t launch_fp8_quant(const void* x, int io, int rows, int K, uint8_t* cod
 hipError_t launch_fp8_linear(const Fp8Linear& p, int out_io, hipStream_t st) {
   if (p.rows <= 0) return hipSuccess;
   if (p.K % 32) return hipErrorInvalidValue;
+  if (fp8_tiled_supported(p)) return launch_fp8_tiled(p, out_io, st);
   if (p.K % kF8K == 0) {
     const dim3 grid((p.N + kF8T - 1) / kF8T, (unsigned)((p.rows + kF8T - 1) / kF8T)), block(256);
     if (out_io == kF32)

@@ -649,6 +649,221 @@ hipError_t dense_tiled_t(const DenseParams& d, bool gelu, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) linear layer, y = dec(a) dec(w)^T * sa[:, None] * sw[None, :] +
+// bias (the codes and per-row scales of fp8.hip), on the same persistent,
+// XCD-contiguous tile walk and direct-to-LDS stages: a 128-byte stage row is
+// one 128-deep step of the 16x16x128 8-bit float products (unit block
+// scales), whose operand lane holds 32 consecutive bytes (two swizzled 16-byte
+// chunks) of one row.  256 x 128 tiles of 4 waves (128 x 64 each), one
+// workgroup per CU (the accumulators and two fragment sets need 320
+// registers); a stage's fragments are read while the previous stage is
+// multiplied.  C^T orientation with the weight rows of each channel-tile pair
+// interleaved, as above: a lane ends with 8 consecutive output channels.
+// ---------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kFp8MaxN = 4096;  // output channels (column scales and bias in LDS)
+
+template <typename TO, int NK>
+__global__ __launch_bounds__(256, 1) void fp8_tiled_kernel(Fp8Linear p) {
+  constexpr int BM = 256;
+  using G = Cfg<BM, 128, 2, 2>;
+  static_assert(NK % 2 == 0 && NK >= kPrefetch, "stage parity and touch distance");
+  __shared__ __attribute__((aligned(1024))) char smem[G::SMEM];
+  __shared__ float swsm[kFp8MaxN], bsm[kFp8MaxN];  // column scales and bias
+  const int rows = (int)p.rows;
+  const int ncol = p.N / 128;
+  const int ntiles = (rows + BM - 1) / BM * ncol;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const uint32_t cb = load_chunk_bytes();
+  const uint32_t rowbytes = (uint32_t)p.K;
+  const TileWalk tw = tile_walk(ntiles);
+  if (tw.count <= 0) return;
+
+  const i32x4 ra = make_rsrc(p.a, (uint32_t)rows * rowbytes);
+  const i32x4 rw = make_rsrc(p.w, (uint32_t)p.N * rowbytes);
+  const uint32_t smem_a = lds_addr(smem);
+  struct Src {
+    uint32_t a, b, touch;
+  };
+  auto src = [&](int tile, Src& sr) {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    const int m0 = rb * BM, n0 = cbk * 128;
+    // Rows past the end read zeros (the buffer resource's bound).
+    sr.a = (uint32_t)(m0 + load_row<G::A_INS>(0)) * rowbytes + cb;
+    sr.b = (uint32_t)(n0 + load_row<G::B_INS>(0)) * rowbytes + cb;
+    sr.touch = (uint32_t)min(m0 + (int)threadIdx.x % BM, rows - 1) * rowbytes;
+  };
+  auto dma = [&](const Src& sr, int buf, int k) {
+    const uint32_t sa = smem_a + buf * G::STAGE, sb = sa + G::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < G::A_INS; ++i)
+      lds_dma16(ra, sa + (wave * G::A_INS + i) * 1024, sr.a, k * 128 + i * 8 * rowbytes);
+#pragma unroll
+    for (int i = 0; i < G::B_INS; ++i)
+      lds_dma16(rw, sb + (wave * G::B_INS + i) * 1024, sr.b, k * 128 + i * 8 * rowbytes);
+  };
+  auto touch = [&](const Src& sr, int k) {
+    lds_dma4(ra, smem_a + 2 * G::STAGE + wave * 256, sr.touch, k * 128);
+  };
+  // A lane's 32 bytes of a stage row: chunks 2 g4 and 2 g4 + 1, each at its
+  // swizzled position (chunk c of row r at c ^ (r % 8)).
+  auto frag = [&](const char* base, int row) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(base + row * 128 + (((2 * g4) ^ (row & 7)) << 4));
+    const uint4 hi =
+        *reinterpret_cast<const uint4*>(base + row * 128 + (((2 * g4 + 1) ^ (row & 7)) << 4));
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                 (int)hi.w};
+  };
+  constexpr int TM = G::TM, TN = G::TN;  // 8 x 4 tiles of 16
+  auto read_frags = [&](int buf, i32x8 (&af)[TM], i32x8 (&bf)[TN]) {
+    const char* sa = smem + buf * G::STAGE + wm * G::WM * 128;
+    const char* sb = smem + buf * G::STAGE + G::A_BYTES + wn * G::WN * 128;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = frag(sa, 16 * i + i16);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bf[j] = frag(sb, 32 * (j >> 1) + 8 * (i16 >> 2) + 4 * (j & 1) + (i16 & 3));
+  };
+  f32x4 acc[TM][TN];
+  TO* y = static_cast<TO*>(p.y);
+  // Published by the prologue's barrier.
+  for (int n = threadIdx.x; n < p.N; n += G::THREADS) {
+    swsm[n] = p.sw[n];
+    bsm[n] = p.bias ? ld_any(p.bias, p.bias_type, n) : 0.f;
+  }
+  // Row scales of a tile, loaded during its last stage (rows clamped, so that
+  // there are always TM loads).
+  float sa[TM];
+  auto load_sa = [&](int tile) {
+    int mbase = (tile / ncol) * BM + wm * G::WM + i16;
+    asm volatile("" : "+v"(mbase));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa[i] = p.sa[min(mbase + 16 * i, rows - 1)];
+  };
+  // Stores per lane of a tile with every row present.
+  constexpr int kStores = TM * (TN / 2) * (sizeof(TO) == 4 ? 2 : 1);
+  auto epi = [&](int tile) -> int {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    int mbase = rb * BM + wm * G::WM + i16;
+    int nbase = cbk * 128 + wn * 64 + 8 * g4;
+    asm volatile("" : "+v"(mbase), "+v"(nbase));
+    int n_st = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = mbase + 16 * i;
+      if (m >= rows) continue;
+      n_st += kStores / TM;
+#pragma unroll
+      for (int jp = 0; jp < TN / 2; ++jp) {
+        const int n0 = nbase + 32 * jp;
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[i][2 * jp][r] * sa[i] * swsm[n0 + r] + bsm[n0 + r];
+          v[4 + r] = acc[i][2 * jp + 1][r] * sa[i] * swsm[n0 + 4 + r] + bsm[n0 + 4 + r];
+        }
+        TO* dst = y + (int64_t)m * p.N + nbase + 32 * jp;
+        if constexpr (sizeof(TO) == 4) {
+          gstore16(dst, uint4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                              __float_as_uint(v[3])});
+          gstore16(dst + 4, uint4{__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                  __float_as_uint(v[6]), __float_as_uint(v[7])});
+        } else {
+          vec8<TO> o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = from_f32<TO>(v[e]);
+          gstore16(dst, __builtin_bit_cast(uint4, o));
+        }
+      }
+    }
+    // The wave's count (EPI in the loop below) only when every lane stored
+    // every row; else -1.
+    return __builtin_amdgcn_readfirstlane(n_st) == kStores && __all(n_st == kStores) ? kStores
+                                                                                     : -1;
+  };
+
+  Src cur, nxt;
+  int tile = tw.first;
+  src(tile, cur);
+  src(tw.count > 1 ? tile + tw.stride : tile, nxt);
+  // Prologue: stage 0 and the touches of stages 2, 3; then stage 1.  Every
+  // stage's loads are followed by exactly one touch, so "stage k+1 landed" is
+  // vmcnt(1) whenever no stores came after (and vmcnt(1) waits for them too).
+  dma(cur, 0, 0);
+  touch(cur, 2);
+  wait_vm<1>();
+  __syncthreads();
+  // Two fragment sets: stage k multiplies set k % 2 while stage k + 1's
+  // fragments are read into the other one.
+  i32x8 a0[TM], b0[TN], a1[TM], b1[TN];
+  read_frags(0, a0, b0);
+  dma(cur, 1, 1);
+  touch(cur, 3);
+  int issued = -1;  // stores of the previous tile's epilogue (see epi)
+  for (int it = 0; it < tw.count; ++it) {
+    const bool more = it + 1 < tw.count;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](int k, const i32x8 (&af)[TM], const i32x8 (&bf)[TN], i32x8 (&an)[TM],
+                    i32x8 (&bn)[TN]) {
+      if (k + 1 < NK || more) {
+        // This wave's loads of the next stage have landed.  At k = 0 they are
+        // followed by the touch, the TM row-scale loads and the previous
+        // epilogue's stores, which may stay in flight (a full tile's count is
+        // exact; otherwise everything is waited for).
+        if (k == 0 && issued == kStores)
+          wait_vm<1 + TM + kStores>();
+        else
+          wait_vm<1>();
+        __syncthreads();  // ... everyone's; and this stage's buffer is free
+        if (k + 2 < NK) dma(cur, k & 1, k + 2);
+        else if (more) dma(nxt, k & 1, k + 2 - NK);
+        if (k + kPrefetch < NK) touch(cur, k + kPrefetch);
+        else touch(more ? nxt : cur, more ? k + kPrefetch - NK : NK - 1);
+        read_frags((k + 1) & 1, an, bn);
+      }
+      if (k == NK - 1) load_sa(tile);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i], acc[i][j], 0,
+                                                                       0, 0, 127, 0, 127);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma nounroll
+    for (int k = 0; k < NK; k += 2) {
+      step(k, a0, b0, a1, b1);
+      step(k + 1, a1, b1, a0, b0);
+    }
+    issued = epi(tile);
+    tile += tw.stride;
+    cur = nxt;
+    if (it + 2 < tw.count) src(tile + tw.stride, nxt);
+  }
+}
+
+template <typename TO>
+hipError_t fp8_tiled_t(const Fp8Linear& p, hipStream_t st) {
+  const int tiles = (int)((p.rows + 255) / 256) * (p.N / 128);
+  const dim3 grid(persistent_grid(tiles, 1)), block(256);
+  switch (p.K) {
+    case 512: hipLaunchKernelGGL((fp8_tiled_kernel<TO, 4>), grid, block, 0, st, p); break;
+    case 1024: hipLaunchKernelGGL((fp8_tiled_kernel<TO, 8>), grid, block, 0, st, p); break;
+    case 1536: hipLaunchKernelGGL((fp8_tiled_kernel<TO, 12>), grid, block, 0, st, p); break;
+    case 2048: hipLaunchKernelGGL((fp8_tiled_kernel<TO, 16>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // The operand buffer resources take 32-bit byte counts and offsets: A (rows x K,
@@ -661,6 +876,22 @@ bool dense_tiled_supported(int64_t rows, int N, int K, int io) {
 hipError_t launch_dense_tiled(const DenseParams& d, bool gelu, hipStream_t st) {
   if (!dense_tiled_supported(d.rows, d.N, d.K, d.io)) return hipErrorInvalidValue;
   return d.io == kF16 ? dense_tiled_t<h16>(d, gelu, st) : dense_tiled_t<b16>(d, gelu, st);
+}
+
+// K in {512, 1024, 1536, 2048} (4 .. 16 steps of 128), N % 128 == 0 and at
+// most kFp8MaxN, both code matrices below 2 GiB, y 16-byte aligned.
+bool fp8_tiled_supported(const Fp8Linear& p) {
+  return p.rows > 0 && p.N % 128 == 0 && p.N <= kFp8MaxN &&
+         (p.K == 512 || p.K == 1024 || p.K == 1536 || p.K == 2048) &&
+         p.rows * p.K < ((int64_t)1 << 31) && (int64_t)p.N * p.K < ((int64_t)1 << 31) &&
+         (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+}
+
+hipError_t launch_fp8_tiled(const Fp8Linear& p, int out_io, hipStream_t st) {
+  if (!fp8_tiled_supported(p)) return hipErrorInvalidValue;
+  if (out_io == kF32) return fp8_tiled_t<float>(p, st);
+  if (out_io == kF16) return fp8_tiled_t<h16>(p, st);
+  return fp8_tiled_t<b16>(p, st);
 }
 
 bool tiled_gemm_supported(int C, int io) { return io != kF32 && (C == 256 || C == 512); }

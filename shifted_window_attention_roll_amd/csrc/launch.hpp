@@ -165,6 +165,9 @@ __device__ __forceinline__ float ld_any(const void* p, int type, int i) {
 hipError_t launch_fp8_quant(const void* x, int io, int rows, int K, uint8_t* codes, float* scales,
                             hipStream_t st);
 hipError_t launch_fp8_linear(const Fp8Linear& p, int out_io, hipStream_t st);
+// The persistent tiled FP8 product (gemm_tiled.hip) where it applies.
+bool fp8_tiled_supported(const Fp8Linear& p);
+hipError_t launch_fp8_tiled(const Fp8Linear& p, int out_io, hipStream_t st);
 
 // 2:4 sparse linear layers (sparse.hip).
 struct Sparse24Linear {

@@ -78,6 +78,10 @@ def _check_linear(got, qa, sa, qw, sw, bias, out_dtype, rows_idx=None):
     (33, 64, 512, "fp32", torch.float32),
     (256, 1536, 512, "bf16", torch.bfloat16),   # QKV of a C = 512 stage
     (70, 512, 2048, "bf16", torch.float32),     # long K
+    # the persistent tiled product (K in 512 .. 2048, N % 128 == 0): several
+    # 256-row tiles per workgroup, a ragged last one
+    (1000, 384, 1024, "fp16", torch.float16),
+    (777, 256, 1536, "bf16", torch.float32),
 ])
 def test_linear(gpu, rows, N, K, in_dtype, out_dtype):
     _say(f"fp8 linear rows={rows} N={N} K={K} {in_dtype} -> {out_dtype}")
