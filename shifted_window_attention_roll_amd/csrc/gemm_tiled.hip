@@ -864,6 +864,235 @@ hipError_t fp8_tiled_t(const Fp8Linear& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// 2:4 structured-sparse linear layer, y = x wp^T + bias (the kept values and
+// positions of sparse.hip), on the same tile walk: a 128-byte token stage row
+// is one 64-deep step of the 16x16x64 sparse products (twice the dense rate),
+// whose token operand lane holds k = 8 g4 .. +7 and 32 + 8 g4 .. +7 (chunks g4
+// and 4 + g4).  Per step the weight side is the kept values (64 bytes a
+// channel, chunks swizzled) and the positions (16 bytes a channel, 4-byte
+// loads), both staged by direct-to-LDS loads with the channels stored
+// permuted so that a fragment reads 16 consecutive rows.  256 tokens x 128
+// channels per tile, 4 waves of 128 x 64, one workgroup per CU, two fragment
+// sets; a lane ends with 8 consecutive output channels of one token.
+// ---------------------------------------------------------------------------
+constexpr int kSpMaxN = 2048;  // output channels (bias in LDS)
+
+// 16-byte chunk q of row r of a 64-byte-row block sits at q ^ sw64(r): the 16
+// consecutive rows of a fragment read then touch distinct bank slots.
+__device__ __forceinline__ int sw64(int r) { return ((r >> 1) ^ (r >> 2) ^ (r >> 4)) & 3; }
+// LDS row of a 128-channel block -> the channel it holds (pairs of 16-channel
+// tiles interleaved: LDS row 16t + 4a + b of a 32-row part holds 8a + 4t + b).
+__device__ __forceinline__ int sp_channel_of_row(int l) {
+  return (l & ~31) | (((l >> 2) & 3) << 3) | (((l >> 4) & 1) << 2) | (l & 3);
+}
+
+template <typename T, int NK>
+__global__ __launch_bounds__(256, 1) void sparse24_tiled2_kernel(Sparse24Linear p) {
+  typedef T v8 __attribute__((ext_vector_type(8)));
+  typedef T v16 __attribute__((ext_vector_type(16)));
+  constexpr int BM = 256, BN = 128, WAVES = 4;
+  static_assert(NK % 2 == 0 && NK >= kPrefetch, "stage parity and touch distance");
+  constexpr int A_BYTES = BM * 128, V_BYTES = BN * 64, C_BYTES = BN * 16;
+  constexpr int STAGE = A_BYTES + V_BYTES + C_BYTES;
+  constexpr int A_INS = BM / 8 / WAVES;          // 1 KB token-row loads per wave and stage
+  constexpr int V_INS = V_BYTES / 1024 / WAVES;  // 1 KB kept-value loads
+  constexpr int C_INS = C_BYTES / 256 / WAVES;   // 256 B position loads (4 bytes a lane)
+  constexpr int TM = 8, TN = 4;                  // 128 tokens x 64 channels per wave
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + WAVES * 256];
+  __shared__ float bsm[kSpMaxN];
+  const int rows = (int)p.rows;
+  const int ncol = p.N / BN;
+  const int ntiles = (rows + BM - 1) / BM * ncol;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const uint32_t cb = load_chunk_bytes();
+  const uint32_t rowbytes = (uint32_t)p.K * 2;  // token rows
+  const uint32_t vbytes = (uint32_t)p.K;        // kept values of a channel
+  const uint32_t cbytes = (uint32_t)p.K / 4;    // positions of a channel
+  const TileWalk tw = tile_walk(ntiles);
+  if (tw.count <= 0) return;
+
+  const i32x4 rx = make_rsrc(p.x, (uint32_t)rows * rowbytes);
+  const i32x4 rv = make_rsrc(p.vals, (uint32_t)p.N * vbytes);
+  const i32x4 rc = make_rsrc(p.codes, (uint32_t)p.N * cbytes);
+  const uint32_t smem_a = lds_addr(smem);
+  // Per-lane source offsets of a tile (stage 0): token rows (linear: the
+  // instruction index adds 8 rows), and the kept values / positions of the
+  // channel each lane's LDS row holds.
+  struct Src {
+    uint32_t a, v[V_INS], c[C_INS], touch;
+  };
+  auto src = [&](int tile, Src& sr) {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    const int m0 = rb * BM, n0 = cbk * BN;
+    sr.a = (uint32_t)(m0 + load_row<A_INS>(0)) * rowbytes + cb;  // rows past the end read 0
+#pragma unroll
+    for (int i = 0; i < V_INS; ++i) {
+      const int l = 16 * (wave * V_INS + i) + (lane >> 2), slot = lane & 3;
+      sr.v[i] = (uint32_t)(n0 + sp_channel_of_row(l)) * vbytes + ((slot ^ sw64(l)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < C_INS; ++i) {
+      const int l = 16 * (wave * C_INS + i) + (lane >> 2);
+      sr.c[i] = (uint32_t)(n0 + sp_channel_of_row(l)) * cbytes + 4 * (lane & 3);
+    }
+    sr.touch = (uint32_t)min(m0 + (int)threadIdx.x % BM, rows - 1) * rowbytes;
+  };
+  auto dma = [&](const Src& sr, int buf, int k) {
+    const uint32_t sa = smem_a + buf * STAGE, sv = sa + A_BYTES, sc = sv + V_BYTES;
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i)
+      lds_dma16(rx, sa + (wave * A_INS + i) * 1024, sr.a, k * 128 + i * 8 * rowbytes);
+#pragma unroll
+    for (int i = 0; i < V_INS; ++i) lds_dma16(rv, sv + (wave * V_INS + i) * 1024, sr.v[i], k * 64);
+#pragma unroll
+    for (int i = 0; i < C_INS; ++i) lds_dma4(rc, sc + (wave * C_INS + i) * 256, sr.c[i], k * 16);
+  };
+  auto touch = [&](const Src& sr, int k) {
+    lds_dma4(rx, smem_a + 2 * STAGE + wave * 256, sr.touch, k * 128);
+  };
+  struct Frags {
+    v16 x[TM];
+    v8 w[TN];
+    int wi[TN];
+  };
+  auto read_frags = [&](int buf, Frags& f) {
+    const char* sa = smem + buf * STAGE + wm * 128 * 128;
+    const char* sv = smem + buf * STAGE + A_BYTES;
+    const char* sc = sv + V_BYTES;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = 16 * i + i16;
+      const v8 lo = *reinterpret_cast<const v8*>(sa + r * 128 + ((g4 ^ (r & 7)) << 4));
+      const v8 hi = *reinterpret_cast<const v8*>(sa + r * 128 + (((4 + g4) ^ (r & 7)) << 4));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        f.x[i][e] = lo[e];
+        f.x[i][8 + e] = hi[e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int l = wn * 64 + 16 * j + i16;
+      f.w[j] = *reinterpret_cast<const v8*>(sv + l * 64 + ((g4 ^ sw64(l)) << 4));
+      const uint32_t c4 = *reinterpret_cast<const uint32_t*>(sc + l * 16 + 4 * g4);
+      // Four groups' positions (p0 | p1 << 2 a byte) as four nibbles.
+      f.wi[j] = (int)((c4 & 0xFu) | ((c4 >> 4) & 0xF0u) | ((c4 >> 8) & 0xF00u) |
+                      ((c4 >> 12) & 0xF000u));
+    }
+  };
+  f32x4 acc[TM][TN];
+  T* y = static_cast<T*>(p.y);
+  const T* bias = static_cast<const T*>(p.bias);
+  for (int n = threadIdx.x; n < p.N; n += 256) bsm[n] = bias ? (float)bias[n] : 0.f;
+  constexpr int kStores = TM * (TN / 2);
+  auto epi = [&](int tile) -> int {
+    const int rb = tile / ncol, cbk = tile - (tile / ncol) * ncol;
+    int mbase = rb * BM + wm * 128 + i16;
+    int nbase = cbk * BN + wn * 64 + 8 * g4;
+    asm volatile("" : "+v"(mbase), "+v"(nbase));
+    int n_st = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = mbase + 16 * i;
+      if (m >= rows) continue;
+      n_st += TN / 2;
+#pragma unroll
+      for (int jp = 0; jp < TN / 2; ++jp) {
+        const int n0 = nbase + 32 * jp;
+        vec8<T> o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          o[r] = from_f32<T>(acc[i][2 * jp][r] + bsm[n0 + r]);
+          o[4 + r] = from_f32<T>(acc[i][2 * jp + 1][r] + bsm[n0 + 4 + r]);
+        }
+        gstore16(y + (int64_t)m * p.N + n0, __builtin_bit_cast(uint4, o));
+      }
+    }
+    return __builtin_amdgcn_readfirstlane(n_st) == kStores && __all(n_st == kStores) ? kStores
+                                                                                     : -1;
+  };
+
+  Src cur, nxt;
+  int tile = tw.first;
+  src(tile, cur);
+  src(tw.count > 1 ? tile + tw.stride : tile, nxt);
+  // Prologue (as in run_tiles): stage 0 and the touches of stages 2, 3; then
+  // stage 1.  Every stage's loads are followed by exactly one touch.
+  dma(cur, 0, 0);
+  touch(cur, 2);
+  wait_vm<1>();
+  __syncthreads();
+  Frags f0, f1;
+  read_frags(0, f0);
+  dma(cur, 1, 1);
+  touch(cur, 3);
+  bool issued_ok = false;  // the previous tile stored every row (see epi)
+  for (int it = 0; it < tw.count; ++it) {
+    const bool more = it + 1 < tw.count;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](int k, const Frags& fc, Frags& fn) {
+      if (k + 1 < NK || more) {
+        // The next stage landed (at k = 0 the previous epilogue's stores
+        // may stay in flight: they follow it, and their count is exact).
+        if (k == 0 && issued_ok)
+          wait_vm<1 + kStores>();
+        else
+          wait_vm<1>();
+        __syncthreads();  // everyone's; and this stage's buffer is free
+        if (k + 2 < NK) dma(cur, k & 1, k + 2);
+        else if (more) dma(nxt, k & 1, k + 2 - NK);
+        if (k + kPrefetch < NK) touch(cur, k + kPrefetch);
+        else touch(more ? nxt : cur, more ? k + kPrefetch - NK : NK - 1);
+        read_frags((k + 1) & 1, fn);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (__is_same(T, h16))
+            acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(fc.w[j], fc.x[i], acc[i][j],
+                                                                 fc.wi[j], 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(fc.w[j], fc.x[i], acc[i][j],
+                                                                  fc.wi[j], 0, 0);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma nounroll
+    for (int k = 0; k < NK; k += 2) {
+      step(k, f0, f1);
+      step(k + 1, f1, f0);
+    }
+    issued_ok = epi(tile) == kStores;
+    tile += tw.stride;
+    cur = nxt;
+    if (it + 2 < tw.count) src(tile + tw.stride, nxt);
+  }
+}
+
+template <typename T>
+hipError_t sparse24_tiled2_t(const Sparse24Linear& p, hipStream_t st) {
+  const int tiles = (int)((p.rows + 255) / 256) * (p.N / 128);
+  const dim3 grid(persistent_grid(tiles, 1)), block(256);
+  switch (p.K) {
+    case 256: hipLaunchKernelGGL((sparse24_tiled2_kernel<T, 4>), grid, block, 0, st, p); break;
+    case 512: hipLaunchKernelGGL((sparse24_tiled2_kernel<T, 8>), grid, block, 0, st, p); break;
+    case 1024: hipLaunchKernelGGL((sparse24_tiled2_kernel<T, 16>), grid, block, 0, st, p); break;
+    case 1536: hipLaunchKernelGGL((sparse24_tiled2_kernel<T, 24>), grid, block, 0, st, p); break;
+    case 2048: hipLaunchKernelGGL((sparse24_tiled2_kernel<T, 32>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // The operand buffer resources take 32-bit byte counts and offsets: A (rows x K,
@@ -892,6 +1121,20 @@ hipError_t launch_fp8_tiled(const Fp8Linear& p, int out_io, hipStream_t st) {
   if (out_io == kF32) return fp8_tiled_t<float>(p, st);
   if (out_io == kF16) return fp8_tiled_t<h16>(p, st);
   return fp8_tiled_t<b16>(p, st);
+}
+
+// K in {256, 512, 1024, 1536, 2048} (4 .. 32 steps of 64), N % 128 == 0 and
+// at most kSpMaxN, 16-bit, every operand below 2 GiB, y 16-byte aligned.
+bool sparse24_tiled2_supported(const Sparse24Linear& p, int io) {
+  return io != kF32 && p.rows > 0 && p.N % 128 == 0 && p.N <= kSpMaxN &&
+         (p.K == 256 || p.K == 512 || p.K == 1024 || p.K == 1536 || p.K == 2048) &&
+         p.rows * p.K * 2 < ((int64_t)1 << 31) && (int64_t)p.N * p.K < ((int64_t)1 << 31) &&
+         (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+}
+
+hipError_t launch_sparse24_tiled2(const Sparse24Linear& p, int io, hipStream_t st) {
+  if (!sparse24_tiled2_supported(p, io)) return hipErrorInvalidValue;
+  return io == kF16 ? sparse24_tiled2_t<h16>(p, st) : sparse24_tiled2_t<b16>(p, st);
 }
 
 bool tiled_gemm_supported(int C, int io) { return io != kF32 && (C == 256 || C == 512); }

@@ -182,6 +182,9 @@ struct Sparse24Linear {
 hipError_t launch_prune24(const void* w, int io, int N, int K, void* vals, uint8_t* codes,
                           hipStream_t st);
 hipError_t launch_sparse24_linear(const Sparse24Linear& p, int io, hipStream_t st);
+// The persistent tiled sparse product (gemm_tiled.hip) where it applies.
+bool sparse24_tiled2_supported(const Sparse24Linear& p, int io);
+hipError_t launch_sparse24_tiled2(const Sparse24Linear& p, int io, hipStream_t st);
 
 inline int max_window(int io_bytes) { return io_bytes == 4 ? 16 : 24; }
 

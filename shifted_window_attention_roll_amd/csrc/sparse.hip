@@ -278,6 +278,7 @@ hipError_t launch_prune24(const void* w, int io, int N, int K, void* vals, uint8
 hipError_t launch_sparse24_linear(const Sparse24Linear& p, int io, hipStream_t st) {
   if (p.rows <= 0) return hipSuccess;
   if (p.K % 64) return hipErrorInvalidValue;
+  if (sparse24_tiled2_supported(p, io)) return launch_sparse24_tiled2(p, io, st);
   if (p.N % 4 == 0 && (reinterpret_cast<uintptr_t>(p.y) & 7) == 0 &&
       (reinterpret_cast<uintptr_t>(p.codes) & 15) == 0 && (p.K / 4) % 16 == 0) {
     const dim3 grid((p.N + kSpT - 1) / kSpT, (unsigned)((p.rows + kSpT - 1) / kSpT)), block(256);

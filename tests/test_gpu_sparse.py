@@ -47,7 +47,10 @@ def test_compress_bit_exact(gpu, N, K, dtype):
 
 @pytest.mark.parametrize("rows,N,K,dtype", [(100, 96, 64, "bf16"), (64, 288, 128, "fp16"),
                                             (50, 90, 128, "fp16"),   # N % 4 != 0: untiled kernel
-                                            (37, 1536, 512, "bf16"), (256, 512, 2048, "fp16")])
+                                            (37, 1536, 512, "bf16"), (256, 512, 2048, "fp16"),
+                                            # the persistent tiled product: several 256-row
+                                            # tiles per workgroup, a ragged last one
+                                            (1000, 384, 1024, "fp16"), (777, 256, 256, "bf16")])
 def test_linear(gpu, rows, N, K, dtype):
     _say(f"sparse24 linear rows={rows} N={N} K={K} {dtype}")
     x = workloads.make_upstream_grad((rows, K), dtype, rows + 3 * K)
@@ -93,4 +96,17 @@ def test_linear_without_bias(gpu):
     wp = sp.prune24(workloads.f64(w))
     ref = sp.linear_sparse24(workloads.f64(x), wp)
     bound = U["fp16"] * np.abs(ref) + 2 * 128 * 2.0 ** -24 * (np.abs(workloads.f64(x)) @ np.abs(wp).T)
+    assert np.all(np.abs(workloads.f64(y.cpu()) - ref) <= bound)
+
+
+def test_linear_without_bias_tiled(gpu):
+    _say("sparse24 linear without bias, persistent tiled product")
+    x = workloads.make_upstream_grad((300, 512), "bf16", 18)
+    w = workloads.make_upstream_grad((256, 512), "bf16", 19, std=0.02)
+    vals, codes = gpu.sparse24_compress(w.cuda())
+    y = gpu.sparse24_linear(x.cuda(), vals, codes, None)
+    torch.cuda.synchronize()
+    wp = sp.prune24(workloads.f64(w))
+    ref = sp.linear_sparse24(workloads.f64(x), wp)
+    bound = U["bf16"] * np.abs(ref) + 2 * 512 * 2.0 ** -24 * (np.abs(workloads.f64(x)) @ np.abs(wp).T)
     assert np.all(np.abs(workloads.f64(y.cpu()) - ref) <= bound)
