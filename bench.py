@@ -23,7 +23,7 @@ Prints ONE JSON line on stdout (logs go to stderr) with:
   full_block   informational: the whole block forward (LayerNorms, attention,
                MLP, residual adds) of each workload's last block,
   backward     informational: the attention sub-layer backward of each
-               workload's last block (windows up to 16; float32 compute),
+               workload's last block (float32 compute),
   fp8_qkv      informational: the FP8 (E4M3) linear layer on each 16-bit
                workload's QKV shape (quantisation and product timed apart),
                and the 2:4-sparse linear layer on the same shape.
@@ -422,8 +422,6 @@ def backward_time(name, steps, warmup):
     import shifted_window_attention_roll_amd as swin
     import workloads
     case = workloads.make_workload(name)
-    if case.M > 16:
-        return None
     blk, dev = case.blocks[-1], "cuda"
     if case.mode == "v1":
         table = blk.table.to(dev)

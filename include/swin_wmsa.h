@@ -64,6 +64,11 @@ const char* swin_status_str(swin_status s);
 /* SWIN_WMSA_ABI_VERSION of the built library. */
 int swin_abi_version(void);
 
+/* The HIP runtime's description of the last HIP error that an entry point
+ * returned as SWIN_ERR_HIP on the calling thread ("no error" before any);
+ * a static string, never NULL.  Kept per thread until the next such error. */
+const char* swin_last_hip_error(void);
+
 /*
  * Cyclic shift + window partition ("Boosting Swin Transformer Speed:
  * Profiling, Mixed Precision, and Kernel Fusion Secrets", Training Optimization:
@@ -258,7 +263,8 @@ swin_status swin_block_fwd(const swin_block_desc* d, const void* x, const swin_b
  *   workspace, ws_bytes >= swin_wmsa_bwd_workspace_size(desc): x and dy in
  *   window order, the recomputed q | k | v and attention output and their
  *   gradients (float32); overwritten by every call.
- * Requires a valid descriptor with M <= 16 (else SWIN_ERR_UNSUPPORTED);
+ * Requires a descriptor valid as for swin_wmsa_fwd, except that M <= 24 for
+ * every dtype (else SWIN_ERR_UNSUPPORTED);
  * x, dy, dx, w_qkv, w_proj and the workspace 16-byte aligned (SWIN_ERR_ALIGN);
  * no output overlapping an input, another output or the workspace
  * (SWIN_ERR_ALIAS); dtau non-NULL in V2.  Computes in float32 throughout.

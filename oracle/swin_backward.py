@@ -48,6 +48,8 @@ def wmsa_backward(x, w_qkv, b_qkv, w_proj, b_proj, bias_table, M: int, s: int, h
 
     Returns a dict with dx [B,H,W,C], dw_qkv [3C,C], db_qkv [3C], dw_proj [C,C],
     db_proj [C], dtable [(2M-1)^2, heads] and (V2) dtau [heads], all float64.
+    V2 also returns dtau_abs [heads]: the same sum over |terms|, which measures
+    how far the signed sum cancels (an error scale for dtau, not a gradient).
     """
     x = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
@@ -124,6 +126,8 @@ def wmsa_backward(x, w_qkv, b_qkv, w_proj, b_proj, bias_table, M: int, s: int, h
         dcos = dlogit / t_eff[None, :, None, None]
         live = tau > tau_min
         out["dtau"] = np.where(live, -(dlogit * cos).sum(axis=(0, 2, 3)) / t_eff ** 2, 0.0)
+        out["dtau_abs"] = np.where(live, np.abs(dlogit * cos).sum(axis=(0, 2, 3)) / t_eff ** 2,
+                                   0.0)
         dqn = dcos @ kn
         dkn = dcos.transpose(0, 1, 3, 2) @ qn
 

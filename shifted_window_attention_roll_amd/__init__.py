@@ -17,9 +17,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libswin_wmsa.so")
 
 SWIN_OK = 0
+SWIN_ERR_HIP = 8
 SWIN_V1, SWIN_V2 = 1, 2
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-_EXPORTS = ("swin_status_str", "swin_abi_version", "swin_partition_shift", "swin_reverse_unshift",
+_EXPORTS = ("swin_status_str", "swin_abi_version", "swin_last_hip_error", "swin_partition_shift", "swin_reverse_unshift",
             "swin_cpb_table", "swin_wmsa_workspace_size", "swin_wmsa_fwd",
             "swin_wmsa_kernel_count", "swin_wmsa_kernel_name", "swin_wmsa_fwd_timed",
             "swin_block_workspace_size", "swin_block_fwd", "swin_wmsa_bwd_workspace_size",
@@ -64,6 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i, f, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int
     lib.swin_status_str.restype = ctypes.c_char_p
+    lib.swin_last_hip_error.restype = ctypes.c_char_p
+    lib.swin_last_hip_error.argtypes = []
     lib.swin_status_str.argtypes = [st]
     lib.swin_abi_version.restype = i
     lib.swin_abi_version.argtypes = []
@@ -118,7 +121,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 class SwinError(RuntimeError):
     def __init__(self, code: int):
         self.code = code
-        super().__init__(load_library().swin_status_str(code).decode())
+        lib = load_library()
+        msg = lib.swin_status_str(code).decode()
+        if code == SWIN_ERR_HIP:
+            msg += " (" + lib.swin_last_hip_error().decode() + ")"
+        super().__init__(msg)
 
 
 def _check(code: int) -> None:

@@ -51,7 +51,7 @@ Geom make_geom(int B, int H, int W, int C, int M, int s, int heads) {
   return g;
 }
 
-swin_status from_hip(hipError_t e) { return e == hipSuccess ? SWIN_OK : SWIN_ERR_HIP; }
+swin_status from_hip(hipError_t e) { return hip_status(e); }
 
 // Storage type of q and k: V2 with 16-bit I/O keeps the normalised, 1/tau-scaled
 // q and k in float16 (|q| <= log2(e)/0.01, |k| <= 1), whose 11-bit significand
@@ -127,7 +127,13 @@ WsLayout ws_layout(const swin_wmsa_desc* d) {
   return L;
 }
 
-swin_status validate_desc(const swin_wmsa_desc* d) {
+// Largest window of the backward: its attention kernel pads a window to at most
+// 576 tokens, whatever the I/O type (it computes in float32).
+constexpr int kBwdMaxWindow = 24;
+
+// Descriptor checks shared by the forward and the backward; max_m is the
+// largest window the caller's kernels take for this descriptor.
+swin_status validate_desc_upto(const swin_wmsa_desc* d, int max_m) {
   if (!d) return SWIN_ERR_NULL;
   if (d->mode != SWIN_V1 && d->mode != SWIN_V2) return SWIN_ERR_DTYPE;
   if (d->dtype != SWIN_F32 && d->dtype != SWIN_F16 && d->dtype != SWIN_BF16) return SWIN_ERR_DTYPE;
@@ -135,8 +141,13 @@ swin_status validate_desc(const swin_wmsa_desc* d) {
   if (st != SWIN_OK) return st;
   if (d->heads < 1 || d->C % d->heads) return SWIN_ERR_SHAPE;
   if (d->C / d->heads != kHeadDim) return SWIN_ERR_UNSUPPORTED;
-  if (d->M > max_window(elem_bytes(d->dtype))) return SWIN_ERR_UNSUPPORTED;
+  if (d->M > max_m) return SWIN_ERR_UNSUPPORTED;
   return SWIN_OK;
+}
+
+swin_status validate_desc(const swin_wmsa_desc* d) {
+  if (!d) return SWIN_ERR_NULL;
+  return validate_desc_upto(d, max_window(elem_bytes(d->dtype)));
 }
 
 }  // namespace
@@ -162,6 +173,8 @@ const char* swin_status_str(swin_status s) {
 }
 
 int swin_abi_version(void) { return SWIN_WMSA_ABI_VERSION; }
+
+const char* swin_last_hip_error(void) { return hipGetErrorString(last_hip_error()); }
 
 static swin_status index_map_common(const void* in, void* out, int B, int H, int W, int C, int M,
                                     int s, swin_dtype dt, void* stream, bool reverse) {
@@ -382,11 +395,15 @@ void* g_scratch[kMaxDevices] = {};
 // device, with that device current).
 swin_status scratch_address(void** out) {
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SWIN_ERR_HIP;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch[dev]) {
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SWIN_ERR_HIP;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess) return hip_status(es);
+    if (!p) return hip_status(hipErrorInvalidSymbol);
     g_scratch[dev] = p;
   }
   *out = g_scratch[dev];
@@ -438,10 +455,7 @@ BwdLayout bwd_layout(const swin_wmsa_desc* d) {
 }
 
 swin_status validate_bwd_desc(const swin_wmsa_desc* d) {
-  swin_status st = validate_desc(d);
-  if (st != SWIN_OK) return st;
-  if (d->M > 16) return SWIN_ERR_UNSUPPORTED;
-  return SWIN_OK;
+  return validate_desc_upto(d, kBwdMaxWindow);
 }
 
 }  // namespace

@@ -189,30 +189,35 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
 // S_ij = c (q_i . k_j) + table[rel(i, j)], c = scale (V1) or 1 / max(tau,
 // tau_min) on unit q, k (V2); masked pairs get the logit kMasked, whose
 // exponential underflows to exactly 0 (the pair (i, i) is always allowed).
-// One workgroup of NP/16 waves per (window, head); N is padded to NP (a multiple
+// One workgroup of WV waves per (window, head); N is padded to NP (a multiple
 // of 32) with zero rows whose label matches only other padding rows, so they
-// stay finite and add nothing.  Wave w owns query tile w (16 rows) for
-// phases 1-3 and key tile w for phase 4.  Products are 16 x 16 tiles
-// (mma_16x16x32: lane l supplies row / column l % 16 and the K-slice
-// 8 (l/16) .. +7; the result holds column l % 16 of rows 4 (l/16) .. +3):
+// stay finite and add nothing.  Wave w owns the TPW = NP / 16 / WV query tiles
+// w TPW .. (16 rows each) for phases 1-3 and the same key tiles for phase 4.
+// Products are 16 x 16 tiles (mma_16x16x32: lane l supplies row / column
+// l % 16 and the K-slice 8 (l/16) .. +7; the result holds column l % 16 of
+// rows 4 (l/16) .. +3):
 //   S = Q K^T, dP = dO V^T (K-slice: head dims, fragments straight from rows);
 //   O = P V, dQ = dS K (K-slice: keys; P and dS go through a per-wave LDS
 //   tile to become row fragments, V and K are read as columns);
 //   S^T = K Q^T, dP^T = V dO^T, dV = P^T dO, dK = dS^T Q (phase 4).
-// LDS rows: K and V for phases 1-3, then Q and dO for phase 4.
+// LDS rows: K and V for phases 1-3, then Q and dO for phase 4, CH rows at a
+// time (all NP when they fit: windows up to 16; window 24 passes them in two
+// chunks per phase, each tile's state kept in registers across the chunks).
 constexpr float kMasked = -1e30f;
 
-template <int NP, bool V2>
-__global__ __launch_bounds__(NP * 4) void attn_bwd_mfma_kernel(AttnBwd p) {
-  constexpr int D = 32, NWV = NP / 16, LD = D + 4;
-  constexpr int TMAX = NP <= 64 ? 15 * 15 : 31 * 31;
-  __shared__ __attribute__((aligned(16))) float b0[NP * LD];   // K, then Q
-  __shared__ __attribute__((aligned(16))) float b1[NP * LD];   // V, then dO
-  __shared__ __attribute__((aligned(16))) float stg[NWV][16 * LD];
+template <int NP, int WV, int CH, bool V2>
+__global__ __launch_bounds__(WV * 64) void attn_bwd_mfma_kernel(AttnBwd p) {
+  constexpr int D = 32, LD = D + 4, NT = WV * 64;
+  constexpr int TPW = NP / 16 / WV, NCH = NP / CH;
+  static_assert(NP % 32 == 0 && (NP / 16) % WV == 0 && NP % CH == 0 && CH % 32 == 0, "split");
+  constexpr int TMAX = NP <= 64 ? 15 * 15 : NP <= 256 ? 31 * 31 : 47 * 47;
+  __shared__ __attribute__((aligned(16))) float b0[CH * LD];   // K, then Q
+  __shared__ __attribute__((aligned(16))) float b1[CH * LD];   // V, then dO
+  __shared__ __attribute__((aligned(16))) float stg[WV][16 * LD];
   __shared__ float rm[NP], rl[NP], rd[NP], nq[NP], nk[NP];
   __shared__ int lab[NP], ra[NP], rb[NP];
   __shared__ float tab[TMAX], dtab[TMAX];
-  __shared__ float red[NWV];
+  __shared__ float red[WV];
 
   const Geom& g = p.g;
   const int M = g.M, N = g.N, C = g.C, R = 2 * M - 1, R2 = R * R;
@@ -233,20 +238,19 @@ __global__ __launch_bounds__(NP * 4) void attn_bwd_mfma_kernel(AttnBwd p) {
   const int wy = wl / g.nWx, wx = wl - wy * g.nWx;
   const bool my = g.s > 0 && wy == g.H / M - 1;
   const bool mx = g.s > 0 && wx == g.nWx - 1;
-  for (int e = t; e < R2; e += NP * 4) {
+  for (int e = t; e < R2; e += NT) {
     tab[e] = p.table[(int64_t)e * g.heads + h];
     dtab[e] = 0.f;
   }
-  // Row t of a 32-float head slice (zeros for padding), V2 norm.
-  auto norm32 = [&](const float* src, float& n) {
+  // V2 norm of a 32-float head slice.
+  auto norm32 = [&](const float* src) {
     float sq = 0.f;
 #pragma unroll
     for (int e = 0; e < D; e += 4) {
       const float4 a = *reinterpret_cast<const float4*>(src + e);
       sq = fmaf(a.x, a.x, fmaf(a.y, a.y, fmaf(a.z, a.z, fmaf(a.w, a.w, sq))));
     }
-    n = sqrtf(sq);
-    return 1.f / fmaxf(n, p.eps);
+    return sqrtf(sq);
   };
   auto copy_row = [&](float* dst, const float* src, float mul) {
 #pragma unroll
@@ -256,24 +260,38 @@ __global__ __launch_bounds__(NP * 4) void attn_bwd_mfma_kernel(AttnBwd p) {
       *reinterpret_cast<float4*>(dst + e) = a;
     }
   };
-  if (t < NP) {
-    const bool real = t < N;
-    const int ty = real ? t / M : M - 1, tx = real ? t - (t / M) * M : M - 1;
-    lab[t] = real ? (my && ty >= M - g.s ? 2 : 0) + (mx && tx >= M - g.s ? 1 : 0) : 99;
-    ra[t] = (ty + M - 1) * R + tx + M - 1;
-    rb[t] = ty * R + tx;
-    const float* row = qkv + (base + t) * 3 * C;
-    float ik = 1.f, iq = 1.f, n0 = 0.f, n1 = 0.f;
-    if (V2 && real) {
-      ik = norm32(row + C, n1);
-      iq = norm32(row, n0);
-    }
-    nq[t] = n0;
-    nk[t] = n1;
-    copy_row(&b0[t * LD], real ? row + C : nullptr, ik);
-    copy_row(&b1[t * LD], real ? row + 2 * C : nullptr, 1.f);
+  // Row labels (region; padding 99), relative-index parts and V2 norms.
+  for (int r = t; r < NP; r += NT) {
+    const bool real = r < N;
+    const int ty = real ? r / M : M - 1, tx = real ? r - (r / M) * M : M - 1;
+    lab[r] = real ? (my && ty >= M - g.s ? 2 : 0) + (mx && tx >= M - g.s ? 1 : 0) : 99;
+    ra[r] = (ty + M - 1) * R + tx + M - 1;
+    rb[r] = ty * R + tx;
+    const float* row = qkv + (base + r) * 3 * C;
+    nq[r] = V2 && real ? norm32(row) : 0.f;
+    nk[r] = V2 && real ? norm32(row + C) : 0.f;
   }
   __syncthreads();
+  auto inv_norm = [&](float n) { return 1.f / fmaxf(n, p.eps); };
+  // Rows c0 .. c0 + CH - 1 of K (unit rows in V2) and V, or of Q and dO.
+  auto load_kv = [&](int c0) {
+    for (int rr = t; rr < CH; rr += NT) {
+      const int r = c0 + rr;
+      const bool real = r < N;
+      const float* row = qkv + (base + r) * 3 * C;
+      copy_row(&b0[rr * LD], real ? row + C : nullptr, V2 && real ? inv_norm(nk[r]) : 1.f);
+      copy_row(&b1[rr * LD], real ? row + 2 * C : nullptr, 1.f);
+    }
+  };
+  auto load_qdo = [&](int c0) {
+    for (int rr = t; rr < CH; rr += NT) {
+      const int r = c0 + rr;
+      const bool real = r < N;
+      const float* row = qkv + (base + r) * 3 * C;
+      copy_row(&b0[rr * LD], real ? row : nullptr, V2 && real ? inv_norm(nq[r]) : 1.f);
+      copy_row(&b1[rr * LD], real ? dout + (base + r) * C : nullptr, 1.f);
+    }
+  };
 
   auto frag_row = [&](const float* r8) {  // 8 consecutive floats of an LDS row
     const float4 a = *reinterpret_cast<const float4*>(r8);
@@ -301,133 +319,159 @@ __global__ __launch_bounds__(NP * 4) void attn_bwd_mfma_kernel(AttnBwd p) {
   auto tidx = [&](int r) { return min(max(r, 0), R2 - 1); };
   float* sw = stg[wave];
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // (query row, key) -> logit, or kMasked across regions.
+  auto logit = [&](float sraw, int q, int key) {
+    return lab[key] == lab[q] ? c * sraw + tab[tidx(ra[q] - rb[key])] : kMasked;
+  };
 
-  // ---- phases 1-3: query tile q0 ----
-  const int q0 = 16 * wave;
+  // ---- phases 1-3: the wave's query tiles ----
+  // A fragments of the wave's query tile u (Q unit rows in V2, dO); reread
+  // per chunk from L2 rather than held across chunks.
+  auto q_frag = [&](int u) {
+    const int qa = 16 * (wave * TPW + u) + i16;
+    const bool real = qa < N;
+    return frag_glob(qkv + (base + qa) * 3 * C, real, V2 && real ? inv_norm(nq[qa]) : 1.f);
+  };
+  auto do_frag = [&](int u) {
+    const int qa = 16 * (wave * TPW + u) + i16;
+    return frag_glob(dout + (base + qa) * C, qa < N, 1.f);
+  };
+  auto qrow_of = [&](int u, int r) { return 16 * (wave * TPW + u) + 4 * g4 + r; };
   float dtau_acc = 0.f;
-  {
-    const int qa = q0 + i16;  // A-fragment row
-    const bool qa_real = qa < N;
-    const float* qrow = qkv + (base + qa) * 3 * C;
-    float qmul = 1.f;
-    if (V2 && qa_real) qmul = 1.f / fmaxf(nq[qa], p.eps);
-    const vec8<float> Qa = frag_glob(qrow, qa_real, qmul);
-    const vec8<float> DOa = frag_glob(dout + (base + qa) * C, qa_real, 1.f);
-    int labr[4], rar[4];
+  if constexpr (NCH == 1) {
+    load_kv(0);
+    __syncthreads();
+  }
+  // Phase 1: online max / sum per row over the lane's key columns, then
+  // across the 16 lanes of the row group.
+  float m[TPW][4], l[TPW][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      labr[r] = lab[q0 + 4 * g4 + r];
-      rar[r] = ra[q0 + 4 * g4 + r];
-    }
-    auto logit = [&](float sraw, int r, int key) {
-      return lab[key] == labr[r] ? c * sraw + tab[tidx(rar[r] - rb[key])] : kMasked;
-    };
-    // Phase 1: online max / sum per row over the lane's key columns, then
-    // across the 16 lanes of the row group.
-    float m[4], l[4];
+  for (int u = 0; u < TPW; ++u)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { m[r] = kMasked; l[r] = 0.f; }
-#pragma unroll 2
-    for (int kt = 0; kt < NWV; ++kt) {
-      const int key = 16 * kt + i16;
-      const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[key * LD + 8 * g4]), zero4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sv = logit(S[r], r, key);
-        const float mn = fmaxf(m[r], sv);
-        l[r] = l[r] * __expf(m[r] - mn) + __expf(sv - mn);
-        m[r] = mn;
-      }
-    }
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float mo = __shfl_xor(m[r], d), lo = __shfl_xor(l[r], d);
-        const float mn = fmaxf(m[r], mo);
-        l[r] = l[r] * __expf(m[r] - mn) + lo * __expf(mo - mn);
-        m[r] = mn;
-      }
-    float il[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) il[r] = 1.f / l[r];
-    // Phase 2: P, dP, D = rowsum(P dP); O = P V.
-    float dacc[4] = {0.f, 0.f, 0.f, 0.f};
-    f32x4 o0 = zero4, o1 = zero4;
+    for (int r = 0; r < 4; ++r) { m[u][r] = kMasked; l[u][r] = 0.f; }
 #pragma unroll 1
-    for (int kb = 0; kb < NP / 32; ++kb) {
+  for (int ch = 0; ch < NCH; ++ch) {
+    if constexpr (NCH > 1) {
+      __syncthreads();  // every wave is done with the previous chunk
+      load_kv(ch * CH);
+      __syncthreads();
+    }
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int key = 32 * kb + 16 * tt + i16;
-        const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[key * LD + 8 * g4]), zero4);
-        const f32x4 dP = mma_16x16x32(DOa, frag_row(&b1[key * LD + 8 * g4]), zero4);
+    for (int u = 0; u < TPW; ++u) {
+      const vec8<float> Qa = q_frag(u);
+#pragma unroll 2
+      for (int kt = 0; kt < CH / 16; ++kt) {
+        const int kl = 16 * kt + i16, key = ch * CH + kl;
+        const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[kl * LD + 8 * g4]), zero4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float pv = __expf(logit(S[r], r, key) - m[r]) * il[r];
-          dacc[r] = fmaf(pv, dP[r], dacc[r]);
-          sw[(4 * g4 + r) * LD + 16 * tt + i16] = pv;
+          const float sv = logit(S[r], qrow_of(u, r), key);
+          const float mn = fmaxf(m[u][r], sv);
+          l[u][r] = l[u][r] * __expf(m[u][r] - mn) + __expf(sv - mn);
+          m[u][r] = mn;
         }
       }
-      asm volatile("" ::: "memory");
-      const vec8<float> Pa = frag_row(&sw[i16 * LD + 8 * g4]);
-      o0 = mma_16x16x32(Pa, frag_col(b1, 32 * kb + 8 * g4, i16), o0);
-      o1 = mma_16x16x32(Pa, frag_col(b1, 32 * kb + 8 * g4, 16 + i16), o1);
-      asm volatile("" ::: "memory");
     }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dacc[r] += __shfl_xor(dacc[r], d);
+      for (int r = 0; r < 4; ++r) {
+        const float mo = __shfl_xor(m[u][r], d), lo = __shfl_xor(l[u][r], d);
+        const float mn = fmaxf(m[u][r], mo);
+        l[u][r] = l[u][r] * __expf(m[u][r] - mn) + lo * __expf(mo - mn);
+        m[u][r] = mn;
+      }
+    if (i16 == 0)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        rm[qrow_of(u, r)] = m[u][r];
+        rl[qrow_of(u, r)] = 1.f / l[u][r];
+      }
+  }
+  __syncthreads();  // row max and inverse sum visible to the row group
+  // Phase 2: P, dP, D = rowsum(P dP); O = P V.
+  float dacc[TPW][4];  // the only per-row state held across chunks, with O
+  f32x4 o0[TPW], o1[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    o0[u] = o1[u] = zero4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dacc[u][r] = 0.f;
+  }
+#pragma unroll 1
+  for (int ch = 0; ch < NCH; ++ch) {
+    if constexpr (NCH > 1) {
+      __syncthreads();
+      load_kv(ch * CH);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const vec8<float> Qa = q_frag(u), DOa = do_frag(u);
+      float mr[4], ilr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mr[r] = rm[qrow_of(u, r)];
+        ilr[r] = rl[qrow_of(u, r)];
+      }
+#pragma unroll 1
+      for (int kb = 0; kb < CH / 32; ++kb) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int kl = 32 * kb + 16 * tt + i16, key = ch * CH + kl;
+          const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[kl * LD + 8 * g4]), zero4);
+          const f32x4 dP = mma_16x16x32(DOa, frag_row(&b1[kl * LD + 8 * g4]), zero4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pv = __expf(logit(S[r], qrow_of(u, r), key) - mr[r]) * ilr[r];
+            dacc[u][r] = fmaf(pv, dP[r], dacc[u][r]);
+            sw[(4 * g4 + r) * LD + 16 * tt + i16] = pv;
+          }
+        }
+        asm volatile("" ::: "memory");
+        const vec8<float> Pa = frag_row(&sw[i16 * LD + 8 * g4]);
+        o0[u] = mma_16x16x32(Pa, frag_col(b1, 32 * kb + 8 * g4, i16), o0[u]);
+        o1[u] = mma_16x16x32(Pa, frag_col(b1, 32 * kb + 8 * g4, 16 + i16), o1[u]);
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dacc[u][r] += __shfl_xor(dacc[u][r], d);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int q = q0 + 4 * g4 + r;
-      if (i16 == 0) {
-        rm[q] = m[r];
-        rl[q] = il[r];
-        rd[q] = dacc[r];
-      }
+      const int q = qrow_of(u, r);
+      if (i16 == 0) rd[q] = dacc[u][r];
       if (q < N) {
         float* og = p.o + (base + q) * C + h * D;
-        og[i16] = o0[r];
-        og[16 + i16] = o1[r];
+        og[i16] = o0[u][r];
+        og[16 + i16] = o1[u][r];
       }
     }
-    // Phase 3: dS = P (dP - D); table (and tau) gradients; dQ = dS K.
-    f32x4 dq0 = zero4, dq1 = zero4;
-#pragma unroll 1
-    for (int kb = 0; kb < NP / 32; ++kb) {
+  }
+  __syncthreads();  // D visible to the row group
+  // Phase 3: dS = P (dP - D); table (and tau) gradients; dQ = dS K.
+  f32x4 dq0[TPW], dq1[TPW];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int key = 32 * kb + 16 * tt + i16;
-        const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[key * LD + 8 * g4]), zero4);
-        const f32x4 dP = mma_16x16x32(DOa, frag_row(&b1[key * LD + 8 * g4]), zero4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = lab[key] == labr[r];
-          const int ti = tidx(rar[r] - rb[key]);
-          const float pv = ok ? __expf(c * S[r] + tab[ti] - m[r]) * il[r] : 0.f;
-          const float ds = pv * (dP[r] - dacc[r]);
-          if (ok) atomicAdd(&dtab[ti], ds);
-          if constexpr (V2) dtau_acc = fmaf(ds, S[r], dtau_acc);
-          sw[(4 * g4 + r) * LD + 16 * tt + i16] = ds;
-        }
-      }
-      asm volatile("" ::: "memory");
-      const vec8<float> Sa = frag_row(&sw[i16 * LD + 8 * g4]);
-      dq0 = mma_16x16x32(Sa, frag_col(b0, 32 * kb + 8 * g4, i16), dq0);
-      dq1 = mma_16x16x32(Sa, frag_col(b0, 32 * kb + 8 * g4, 16 + i16), dq1);
-      asm volatile("" ::: "memory");
-    }
-    // dq (lane: dims i16 and 16 + i16 of rows q0 + 4 g4 + r).
+  for (int u = 0; u < TPW; ++u) dq0[u] = dq1[u] = zero4;
+  // dq of tile u (lane: dims i16 and 16 + i16 of the tile's rows 4 g4 + r).
+  auto store_dq = [&](int u, f32x4 d0, f32x4 d1) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int q = q0 + 4 * g4 + r;
-      float a0 = c * dq0[r], a1 = c * dq1[r];
+      const int q = qrow_of(u, r);
+      float a0 = c * d0[r], a1 = c * d1[r];
       if constexpr (V2) {
         // Through q_hat = q / max(|q|, eps): (dq_hat - q_hat (q_hat . dq_hat)) / |q|.
         const bool real = q < N;
         const float* qr = qkv + (base + (real ? q : 0)) * 3 * C;
-        const float inv = 1.f / fmaxf(nq[q], p.eps);
+        const float inv = inv_norm(nq[q]);
         const float h0 = real ? qr[i16] * inv : 0.f, h1 = real ? qr[16 + i16] * inv : 0.f;
         float pr = h0 * a0 + h1 * a1;
 #pragma unroll
@@ -442,78 +486,73 @@ __global__ __launch_bounds__(NP * 4) void attn_bwd_mfma_kernel(AttnBwd p) {
         dg[16 + i16] = a1;
       }
     }
-  }
-  __syncthreads();  // K, V no longer read; row statistics complete
-  if (t < NP) {
-    const bool real = t < N;
-    const float* row = qkv + (base + t) * 3 * C;
-    copy_row(&b0[t * LD], real ? row : nullptr, V2 && real ? 1.f / fmaxf(nq[t], p.eps) : 1.f);
-    copy_row(&b1[t * LD], real ? dout + (base + t) * C : nullptr, 1.f);
-  }
-  __syncthreads();
-
-  // ---- phase 4: key tile k0 ----
-  {
-    const int k0 = 16 * wave;
-    const int ka = k0 + i16;
-    const bool ka_real = ka < N;
-    const float* krow = qkv + (base + ka) * 3 * C;
-    float kmul = 1.f;
-    if (V2 && ka_real) kmul = 1.f / fmaxf(nk[ka], p.eps);
-    const vec8<float> Ka = frag_glob(krow + C, ka_real, kmul);
-    const vec8<float> Va = frag_glob(krow + 2 * C, ka_real, 1.f);
-    int labr[4], rbr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      labr[r] = lab[k0 + 4 * g4 + r];
-      rbr[r] = rb[k0 + 4 * g4 + r];
-    }
-    f32x4 dk0 = zero4, dk1 = zero4, dv0 = zero4, dv1 = zero4;
+  };
 #pragma unroll 1
-    for (int qb = 0; qb < NP / 32; ++qb) {
-      float pst[2][4], dst[2][4];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int q = 32 * qb + 16 * tt + i16;  // this lane's query column
-        const f32x4 ST = mma_16x16x32(Ka, frag_row(&b0[q * LD + 8 * g4]), zero4);
-        const f32x4 dPT = mma_16x16x32(Va, frag_row(&b1[q * LD + 8 * g4]), zero4);
-        const float mq = rm[q], ilq = rl[q], dq_ = rd[q];
-        const int labq = lab[q], raq = ra[q];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = labq == labr[r];
-          const float pv = ok ? __expf(c * ST[r] + tab[tidx(raq - rbr[r])] - mq) * ilq : 0.f;
-          pst[tt][r] = pv;
-          dst[tt][r] = pv * (dPT[r] - dq_);
-        }
-      }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sw[(4 * g4 + r) * LD + 16 * tt + i16] = pst[tt][r];
-      asm volatile("" ::: "memory");
-      const vec8<float> Pa = frag_row(&sw[i16 * LD + 8 * g4]);
-      dv0 = mma_16x16x32(Pa, frag_col(b1, 32 * qb + 8 * g4, i16), dv0);
-      dv1 = mma_16x16x32(Pa, frag_col(b1, 32 * qb + 8 * g4, 16 + i16), dv1);
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sw[(4 * g4 + r) * LD + 16 * tt + i16] = dst[tt][r];
-      asm volatile("" ::: "memory");
-      const vec8<float> Sa = frag_row(&sw[i16 * LD + 8 * g4]);
-      dk0 = mma_16x16x32(Sa, frag_col(b0, 32 * qb + 8 * g4, i16), dk0);
-      dk1 = mma_16x16x32(Sa, frag_col(b0, 32 * qb + 8 * g4, 16 + i16), dk1);
-      asm volatile("" ::: "memory");
+  for (int ch = 0; ch < NCH; ++ch) {
+    if constexpr (NCH > 1) {
+      __syncthreads();
+      load_kv(ch * CH);
+      __syncthreads();
     }
 #pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const vec8<float> Qa = q_frag(u), DOa = do_frag(u);
+      float mr[4], ilr[4], dr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mr[r] = rm[qrow_of(u, r)];
+        ilr[r] = rl[qrow_of(u, r)];
+        dr[r] = rd[qrow_of(u, r)];
+      }
+#pragma unroll 1
+      for (int kb = 0; kb < CH / 32; ++kb) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int kl = 32 * kb + 16 * tt + i16, key = ch * CH + kl;
+          const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[kl * LD + 8 * g4]), zero4);
+          const f32x4 dP = mma_16x16x32(DOa, frag_row(&b1[kl * LD + 8 * g4]), zero4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = qrow_of(u, r);
+            const bool ok = lab[key] == lab[q];
+            const int ti = tidx(ra[q] - rb[key]);
+            const float pv = ok ? __expf(c * S[r] + tab[ti] - mr[r]) * ilr[r] : 0.f;
+            const float ds = pv * (dP[r] - dr[r]);
+            if (ok) atomicAdd(&dtab[ti], ds);
+            if constexpr (V2) dtau_acc = fmaf(ds, S[r], dtau_acc);
+            sw[(4 * g4 + r) * LD + 16 * tt + i16] = ds;
+          }
+        }
+        asm volatile("" ::: "memory");
+        const vec8<float> Sa = frag_row(&sw[i16 * LD + 8 * g4]);
+        dq0[u] = mma_16x16x32(Sa, frag_col(b0, 32 * kb + 8 * g4, i16), dq0[u]);
+        dq1[u] = mma_16x16x32(Sa, frag_col(b0, 32 * kb + 8 * g4, 16 + i16), dq1[u]);
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) store_dq(u, dq0[u], dq1[u]);
+  __syncthreads();  // K, V no longer read; row statistics complete
+  if constexpr (NCH == 1) {
+    load_qdo(0);
+    __syncthreads();
+  }
+
+  // ---- phase 4: the wave's key tiles ----
+  f32x4 dk0[TPW], dk1[TPW], dv0[TPW], dv1[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) dk0[u] = dk1[u] = dv0[u] = dv1[u] = zero4;
+  // dk, dv of key tile u.
+  auto store_dkv = [&](int u, f32x4 k0, f32x4 k1, f32x4 v0, f32x4 v1) {
+#pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int k = k0 + 4 * g4 + r;
-      float a0 = c * dk0[r], a1 = c * dk1[r];
+      const int k = qrow_of(u, r);
+      float a0 = c * k0[r], a1 = c * k1[r];
       if constexpr (V2) {
         const bool real = k < N;
         const float* kr = qkv + (base + (real ? k : 0)) * 3 * C + C;
-        const float inv = 1.f / fmaxf(nk[k], p.eps);
+        const float inv = inv_norm(nk[k]);
         const float h0 = real ? kr[i16] * inv : 0.f, h1 = real ? kr[16 + i16] * inv : 0.f;
         float pr = h0 * a0 + h1 * a1;
 #pragma unroll
@@ -526,12 +565,69 @@ __global__ __launch_bounds__(NP * 4) void attn_bwd_mfma_kernel(AttnBwd p) {
         float* dg = p.dqkv + (base + k) * 3 * C + C + h * D;
         dg[i16] = a0;
         dg[16 + i16] = a1;
-        dg[C + i16] = dv0[r];
-        dg[C + 16 + i16] = dv1[r];
+        dg[C + i16] = v0[r];
+        dg[C + 16 + i16] = v1[r];
+      }
+    }
+  };
+#pragma unroll 1
+  for (int ch = 0; ch < NCH; ++ch) {
+    if constexpr (NCH > 1) {
+      __syncthreads();
+      load_qdo(ch * CH);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int ka = 16 * (wave * TPW + u) + i16;
+      const bool ka_real = ka < N;
+      const float* krow = qkv + (base + ka) * 3 * C;
+      const vec8<float> Ka = frag_glob(krow + C, ka_real, V2 && ka_real ? inv_norm(nk[ka]) : 1.f);
+      const vec8<float> Va = frag_glob(krow + 2 * C, ka_real, 1.f);
+#pragma unroll 1
+      for (int qb = 0; qb < CH / 32; ++qb) {
+        float pst[2][4], dst[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int ql = 32 * qb + 16 * tt + i16, q = ch * CH + ql;  // this lane's query column
+          const f32x4 ST = mma_16x16x32(Ka, frag_row(&b0[ql * LD + 8 * g4]), zero4);
+          const f32x4 dPT = mma_16x16x32(Va, frag_row(&b1[ql * LD + 8 * g4]), zero4);
+          const float mq = rm[q], ilq = rl[q], dq_ = rd[q];
+          const int labq = lab[q], raq = ra[q];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int k = qrow_of(u, r);
+            const bool ok = labq == lab[k];
+            const float pv = ok ? __expf(c * ST[r] + tab[tidx(raq - rb[k])] - mq) * ilq : 0.f;
+            pst[tt][r] = pv;
+            dst[tt][r] = pv * (dPT[r] - dq_);
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sw[(4 * g4 + r) * LD + 16 * tt + i16] = pst[tt][r];
+        asm volatile("" ::: "memory");
+        const vec8<float> Pa = frag_row(&sw[i16 * LD + 8 * g4]);
+        dv0[u] = mma_16x16x32(Pa, frag_col(b1, 32 * qb + 8 * g4, i16), dv0[u]);
+        dv1[u] = mma_16x16x32(Pa, frag_col(b1, 32 * qb + 8 * g4, 16 + i16), dv1[u]);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sw[(4 * g4 + r) * LD + 16 * tt + i16] = dst[tt][r];
+        asm volatile("" ::: "memory");
+        const vec8<float> Sa = frag_row(&sw[i16 * LD + 8 * g4]);
+        dk0[u] = mma_16x16x32(Sa, frag_col(b0, 32 * qb + 8 * g4, i16), dk0[u]);
+        dk1[u] = mma_16x16x32(Sa, frag_col(b0, 32 * qb + 8 * g4, 16 + i16), dk1[u]);
+        asm volatile("" ::: "memory");
       }
     }
   }
-  for (int e = t; e < R2; e += NP * 4) atomicAdd(p.dtable + (int64_t)e * g.heads + h, dtab[e]);
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) store_dkv(u, dk0[u], dk1[u], dv0[u], dv1[u]);
+  __syncthreads();  // every wave's table-gradient adds are in dtab
+  for (int e = t; e < R2; e += NT) atomicAdd(p.dtable + (int64_t)e * g.heads + h, dtab[e]);
   if constexpr (V2) {
     float v = dtau_acc;
 #pragma unroll
@@ -540,18 +636,20 @@ __global__ __launch_bounds__(NP * 4) void attn_bwd_mfma_kernel(AttnBwd p) {
     __syncthreads();
     if (t == 0 && p.tau[h] > p.tau_min) {
       float sum = 0.f;
-      for (int k = 0; k < NWV; ++k) sum += red[k];
+      for (int k = 0; k < WV; ++k) sum += red[k];
       atomicAdd(p.dtau + h, -sum / (t_eff * t_eff));
     }
   }
 }
 
-template <int NP>
+template <int NP, int WV, int CH>
 void attn_bwd_launch(const AttnBwd& p, bool v2, int items, hipStream_t st) {
   if (v2)
-    hipLaunchKernelGGL((attn_bwd_mfma_kernel<NP, true>), dim3(items), dim3(4 * NP), 0, st, p);
+    hipLaunchKernelGGL((attn_bwd_mfma_kernel<NP, WV, CH, true>), dim3(items), dim3(64 * WV), 0, st,
+                       p);
   else
-    hipLaunchKernelGGL((attn_bwd_mfma_kernel<NP, false>), dim3(items), dim3(4 * NP), 0, st, p);
+    hipLaunchKernelGGL((attn_bwd_mfma_kernel<NP, WV, CH, false>), dim3(items), dim3(64 * WV), 0,
+                       st, p);
 }
 
 template <typename TA, typename TB, typename TC, bool ATOMIC>
@@ -632,10 +730,11 @@ hipError_t backward(const BwdArgs& a, hipStream_t st) {
   p.qkv = a.qkv; p.dout = a.dout; p.table = a.table; p.tau = a.tau;
   p.o = a.o; p.dqkv = a.dqkv; p.dtable = a.dtable; p.dtau = a.dtau;
   const int items = g.B * g.nW * g.heads;
-  if (g.N <= 32) attn_bwd_launch<32>(p, a.v2, items, st);
-  else if (g.N <= 64) attn_bwd_launch<64>(p, a.v2, items, st);
-  else if (g.N <= 128) attn_bwd_launch<128>(p, a.v2, items, st);
-  else attn_bwd_launch<256>(p, a.v2, items, st);
+  if (g.N <= 32) attn_bwd_launch<32, 2, 32>(p, a.v2, items, st);
+  else if (g.N <= 64) attn_bwd_launch<64, 4, 64>(p, a.v2, items, st);
+  else if (g.N <= 128) attn_bwd_launch<128, 8, 128>(p, a.v2, items, st);
+  else if (g.N <= 256) attn_bwd_launch<256, 16, 256>(p, a.v2, items, st);
+  else attn_bwd_launch<576, 12, 288>(p, a.v2, items, st);  // windows up to 24
   TRY(hipGetLastError());
   // dWp = dyw^T o   [C, C];  dbp = column sums of dyw
   BwdGemm wp{};
@@ -667,7 +766,8 @@ hipError_t backward(const BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t st) {
-  if (a.g.M > 16 || a.g.C != 32 * a.g.heads) return hipErrorInvalidValue;
+  // The attention kernel pads a window to at most 576 tokens (window 24).
+  if (a.g.M > 24 || a.g.C != 32 * a.g.heads) return hipErrorInvalidValue;
   if (a.io == kF32) return backward<float>(a, st);
   if (a.io == kF16) return backward<h16>(a, st);
   return backward<b16>(a, st);

@@ -535,7 +535,6 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-swin_status hip_status(hipError_t e) { return e == hipSuccess ? SWIN_OK : SWIN_ERR_HIP; }
 
 template <typename T>
 swin_status block_run(const swin_block_desc* d, const T* x, const swin_block_params* p, T* y,

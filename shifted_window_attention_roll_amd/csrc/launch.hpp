@@ -4,8 +4,23 @@
 #include <hip/hip_runtime.h>
 
 #include "common.hpp"
+#include "swin_wmsa.h"
 
 namespace swin {
+
+// The calling thread's last HIP error that an entry point returned as
+// SWIN_ERR_HIP (hipSuccess until one does).
+inline hipError_t& last_hip_error() {
+  static thread_local hipError_t e = hipSuccess;
+  return e;
+}
+
+// SWIN_OK for hipSuccess, else SWIN_ERR_HIP with the error recorded.
+inline swin_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return SWIN_OK;
+  last_hip_error() = e;
+  return SWIN_ERR_HIP;
+}
 
 // Element type of x / y / weights: 0 = float32, 1 = float16, 2 = bfloat16.
 enum IoType { kF32 = 0, kF16 = 1, kBF16 = 2 };

@@ -43,6 +43,9 @@ def test_abi_version_and_status_strings(lib):
         s = lib.swin_status_str(code).decode()
         assert s.startswith("SWIN_")
     assert lib.swin_status_str(99).decode() == "unknown swin_status"
+    # no HIP error recorded yet on this thread: the runtime's text for success
+    assert lib.swin_last_hip_error().decode()
+    assert str(swin.SwinError(swin.SWIN_ERR_HIP)).startswith("SWIN_ERR_HIP: ")
 
 
 def _desc(**kw):
@@ -272,13 +275,15 @@ def test_bwd_workspace_size(lib):
     parts = [T * C * 2] * 3 + [T * 3 * C * 4, T * C * 4, T * C * 4, T * 3 * C * 4]
     assert swin.bwd_workspace_size(d) == sum((p + 255) // 256 * 256 for p in parts)
     assert swin.bwd_workspace_size(_desc(B=0)) == 0
-    assert swin.bwd_workspace_size(_desc(H=48, W=48, M=24, s=0, dtype=torch.bfloat16)) == 0
+    assert swin.bwd_workspace_size(_desc(H=48, W=48, M=24, s=0, dtype=torch.bfloat16)) > 0
+    assert swin.bwd_workspace_size(_desc(H=48, W=48, M=24, s=0, dtype=torch.float32)) > 0
+    assert swin.bwd_workspace_size(_desc(H=50, W=50, M=25, s=0, dtype=torch.bfloat16)) == 0
     assert swin.bwd_workspace_size(_desc(heads=1)) == 0
 
 
 def test_bwd_rejects_before_launch(lib):
     d = _desc(B=1)
-    assert _bwd(lib, _desc(B=1, H=48, W=48, M=24, s=0, dtype=torch.bfloat16)) == UNSUP
+    assert _bwd(lib, _desc(B=1, H=50, W=50, M=25, s=0, dtype=torch.bfloat16)) == UNSUP
     assert _bwd(lib, _desc(B=1, heads=5)) == SHAPE
     assert _bwd(lib, d, wq=None) == NULL
     assert _bwd(lib, d, dy=None) == NULL

@@ -4,7 +4,10 @@ against the float64 backward oracle on the same seeded inputs.
 Bar (derived; every step runs in float32 on inputs that the oracle takes
 exactly): per gradient tensor, max |gpu - oracle| <= 1e-4 x max |oracle| and
 relative L2 <= 1e-4; the 16-bit dx is also rounded once on output, which adds
-u |oracle| per element (u = 2^-8 bfloat16, 2^-11 float16).
+u |oracle| per element (u = 2^-8 bfloat16, 2^-11 float16).  dtau is one sum of
+B nW N^2 products per head whose terms cancel (by a factor near 2e4 at window
+24): each term carries float32 rounding, so its bar adds 2 x 2^-24 x the sum of
+|terms| (the oracle's dtau_abs) instead of a relative-L2 test.
 """
 import sys
 
@@ -67,11 +70,14 @@ def _assert_grads(g, ref, dtype, mode, what):
         scale = max(float(np.abs(r).max()), 1e-30)
         err = np.abs(got - r)
         bound = TOL * scale + (ULP[dtype] * np.abs(r) if k == "dx" else 0.0)
+        if k == "dtau":
+            bound = bound + 2.0 * 2.0 ** -24 * ref["dtau_abs"]
         worst = float((err - bound).max())
         rel = float(np.linalg.norm(got - r) / max(np.linalg.norm(r), 1e-30))
         _say(f"  {what} {k}: max err {err.max():.3g} (scale {scale:.3g}), rel-L2 {rel:.3g}")
         assert worst <= 0, (what, k, float(err.max()), scale)
-        assert rel <= TOL + 2 * ULP[dtype] * (k == "dx"), (what, k, rel)
+        if k != "dtau":
+            assert rel <= TOL + 2 * ULP[dtype] * (k == "dx"), (what, k, rel)
 
 
 CASES = [
@@ -88,6 +94,10 @@ CASES = [
     (1, 7, 7, 32, 1, 7, 3, "fp32", "v2"),       # window = image, shifted
     (1, 20, 30, 64, 2, 10, 5, "fp32", "v1"),    # window 10: 100 tokens padded to 128
     (2, 12, 12, 64, 2, 3, 1, "fp32", "v2"),     # window 3: 9 tokens padded to 32
+    (1, 48, 48, 64, 2, 24, 12, "fp32", "v1"),   # window 24: two 288-row chunks per phase
+    (1, 48, 24, 32, 1, 24, 7, "bf16", "v2"),    # window 24, odd split, 16-bit I/O
+    (1, 34, 17, 64, 2, 17, 8, "fp32", "v2"),    # window 17: 289 tokens, ragged last tile
+    (1, 40, 20, 32, 1, 20, 0, "fp16", "v1"),    # window 20 unshifted: 400 tokens of 576
 ]
 
 

@@ -80,6 +80,9 @@ def test_v2_clamped_tau_has_zero_gradient():
     g = sbw.wmsa_backward(p["x"], p["w_qkv"], p["b_qkv"], p["w_proj"], p["b_proj"], p["table"],
                           4, 2, 2, dy, "v2", tau=p["tau"])
     assert g["dtau"][1] == 0.0 and g["dtau"][0] != 0.0
+    # the error scale of dtau: the same sum over |terms| bounds it, and is zero
+    # where the clamp is flat
+    assert g["dtau_abs"][1] == 0.0 and g["dtau_abs"][0] >= abs(g["dtau"][0]) > 0.0
 
 
 @pytest.mark.parametrize("mode", ["v1", "v2"])
