@@ -267,7 +267,10 @@ swin_status swin_block_fwd(const swin_block_desc* d, const void* x, const swin_b
  * every dtype (else SWIN_ERR_UNSUPPORTED);
  * x, dy, dx, w_qkv, w_proj and the workspace 16-byte aligned (SWIN_ERR_ALIGN);
  * no output overlapping an input, another output or the workspace
- * (SWIN_ERR_ALIAS); dtau non-NULL in V2.  Computes in float32 throughout.
+ * (SWIN_ERR_ALIAS); dtau non-NULL in V2.  Intermediates and sums in float32;
+ * the GEMMs on 16-bit matrix cores with float32 accumulation (exact products
+ * when both operands share a 16-bit type, else each operand as two bfloat16
+ * terms, about 2^-16 relative per product); the attention on float32 products.
  */
 typedef struct {
   void* dx;        /* [B, H, W, C], desc->dtype                      */

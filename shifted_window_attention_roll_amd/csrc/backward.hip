@@ -18,6 +18,7 @@
 //                                                                   index map)
 // The inverse of a permutation is its adjoint, so the index maps of the
 // forward carry the gradients between the image and window orders.
+#include "kv_frag.hpp"
 #include "launch.hpp"
 
 namespace swin {
@@ -54,19 +55,57 @@ __device__ __forceinline__ void store_row8(float* d, const float (&v)[8]) {
   *reinterpret_cast<float4*>(d + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// C[m][n] (+)= sum_k A(m, k) B(k, n) (+ bias[n]) with element strides, float32
-// on the matrix cores (16x16x4 float32 products, eight per 32-deep step).
-// 64 x 64 tile per workgroup of 4 waves, 32 x 32 per wave; K in steps of 32
-// through LDS, both operands stored [row][k] (k contiguous) so that a lane's
-// fragment is two 16-byte reads; blockIdx.z takes the K range [z*kc,
+// Matrix-core type of a product of TA and TB elements: float16 when both are
+// float16 (each product exact in float32), else bfloat16.
+template <typename TA, typename TB>
+using mma_type_t = typename std::conditional<std::is_same<TA, h16>::value &&
+                                                 std::is_same<TB, h16>::value,
+                                             h16, b16>::type;
+
+// Terms of the product type per operand element: one when the element type is
+// the product type, else two, hi = MT(x) and lo = MT(x - hi) (x - hi is exact
+// in float32).  hi + lo equals a float16 x exactly and a float x to about
+// 2^-17 relative.
+template <typename T, typename MT>
+constexpr int terms_of() {
+  return std::is_same<T, MT>::value ? 1 : 2;
+}
+
+template <typename MT, int P>
+__device__ __forceinline__ void split8(const float (&v)[8], vec8<MT> (&t)[P]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const MT hi = from_f32<MT>(v[e]);
+    t[0][e] = hi;
+    if constexpr (P == 2) t[1][e] = from_f32<MT>(v[e] - (float)hi);
+  }
+}
+
+// C[m][n] (+)= sum_k A(m, k) B(k, n) (+ bias[n]) with element strides, on the
+// 16-bit matrix cores with float32 accumulation (16x16x32 products).  With two
+// terms per operand the product of a pair is hi_a hi_b + hi_a lo_b + lo_a hi_b
+// (lo_a lo_b, about 2^-18 of it, left out): about 2^-16 relative per product
+// for float operands, against 2^-24 for a float32 product.  64 x 64 tile per
+// workgroup of 4 waves, 32 x 32 per wave; K in steps of 32 through LDS, the
+// next step's global loads in flight during the current step's products.
+// Each thread stages runs of 8 elements along an operand's unit stride with
+// one 16-byte store per term: an operand whose unit stride is k is stored
+// [row][k] (80-byte rows: the fragment reads of 8 consecutive rows hit
+// distinct bank groups) and read as rows; one whose unit stride is its row
+// index is stored [k][row] (144-byte rows) and read by transposing loads, which
+// give the lane of fragment row 4a + b of 32-row pair half t the row 8a + 4t +
+// b (undone in the epilogue).  blockIdx.z takes the K range [z*kc,
 // (z+1)*kc).  ATOMIC adds the tile into C (float) instead of storing it; then
 // only z = 0 adds bias.
-constexpr int kGT = 64, kGK = 32, kGP = kGK + 4;
+constexpr int kGT = 64, kGK = 32, kGP = kGK + 8, kTP = kGT + 8;
+static_assert(kGK * kTP <= kGT * kGP, "one plane size for both layouts");
 
 template <typename TA, typename TB, typename TC, bool ATOMIC>
 __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm a) {
-  __shared__ __attribute__((aligned(16))) float As[kGT * kGP];  // [m][k]
-  __shared__ __attribute__((aligned(16))) float Bs[kGT * kGP];  // [n][k]
+  using MT = mma_type_t<TA, TB>;
+  constexpr int PA = terms_of<TA, MT>(), PB = terms_of<TB, MT>();
+  __shared__ __attribute__((aligned(16))) MT As[PA][kGT * kGP];  // [m][k] per term
+  __shared__ __attribute__((aligned(16))) MT Bs[PB][kGT * kGP];  // [n][k] per term
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int i16 = lane & 15, g4 = lane >> 4;
@@ -84,87 +123,127 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(BwdGemm a) {
   // staged runs of the first column tile's workgroups.
   const bool rows_sum = ATOMIC && a.rowsum && !a_k_unit && blockIdx.x == 0;
   float rs[8] = {};
-  for (int64_t kb = k0; kb < k1; kb += kGK) {
-    // Each thread stages one run of 8 elements of each operand along its
-    // unit-stride dimension (k, or the row dimension m / n).
-    {
-      float v[8];
-      if (a_k_unit) {
-        const int mm = tid >> 2, kk = (tid & 3) * 8;
-        const int64_t m = m0 + mm, k = kb + kk;
-        load_run8(A, m * a.sam + k, m < a.M ? (int)min<int64_t>(k1 - k, 8) : 0, v);
-        store_row8(&As[mm * kGP + kk], v);
-      } else {
-        const int kk = tid >> 3, mm = (tid & 7) * 8;
-        const int64_t m = m0 + mm, k = kb + kk;
-        load_run8(A, m + k * a.sak, k < k1 ? (int)min<int64_t>(a.M - m, 8) : 0, v);
+  // Each thread loads one run of 8 elements of each operand along its
+  // unit-stride dimension (k, or the row dimension m / n) of step kb.
+  float va[8], vb[8];
+  auto load = [&](int64_t kb) {
+    if (a_k_unit) {
+      const int mm = tid >> 2, kk = (tid & 3) * 8;
+      const int64_t m = m0 + mm, k = kb + kk;
+      load_run8(A, m * a.sam + k, m < a.M ? (int)min<int64_t>(k1 - k, 8) : 0, va);
+    } else {
+      const int kk = tid >> 3, mm = (tid & 7) * 8;
+      const int64_t m = m0 + mm, k = kb + kk;
+      load_run8(A, m + k * a.sak, k < k1 ? (int)min<int64_t>(a.M - m, 8) : 0, va);
+    }
+    if (!b_n_unit) {
+      const int nn = tid >> 2, kk = (tid & 3) * 8;
+      const int n = n0 + nn;
+      const int64_t k = kb + kk;
+      load_run8(B, (int64_t)n * a.sbn + k, n < a.N ? (int)min<int64_t>(k1 - k, 8) : 0, vb);
+    } else {
+      const int kk = tid >> 3, nn = (tid & 7) * 8;
+      const int n = n0 + nn;
+      const int64_t k = kb + kk;
+      load_run8(B, n + k * a.sbk, k < k1 ? (int)min<int64_t>(a.N - n, 8) : 0, vb);
+    }
+  };
+  // The loaded runs, split into their terms, into LDS.
+  auto stage = [&]() {
+    vec8<MT> ta[PA], tb[PB];
+    split8<MT, PA>(va, ta);
+    split8<MT, PB>(vb, tb);
+    if (a_k_unit) {
+      const int mm = tid >> 2, kk = (tid & 3) * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) As[(mm + i) * kGP + kk] = v[i];
-        if (rows_sum) {
+      for (int p = 0; p < PA; ++p) *reinterpret_cast<vec8<MT>*>(&As[p][mm * kGP + kk]) = ta[p];
+    } else {
+      const int kk = tid >> 3, mm = (tid & 7) * 8;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) rs[i] += v[i];
-        }
-      }
-      if (!b_n_unit) {
-        const int nn = tid >> 2, kk = (tid & 3) * 8;
-        const int n = n0 + nn;
-        const int64_t k = kb + kk;
-        load_run8(B, (int64_t)n * a.sbn + k, n < a.N ? (int)min<int64_t>(k1 - k, 8) : 0, v);
-        store_row8(&Bs[nn * kGP + kk], v);
-      } else {
-        const int kk = tid >> 3, nn = (tid & 7) * 8;
-        const int n = n0 + nn;
-        const int64_t k = kb + kk;
-        load_run8(B, n + k * a.sbk, k < k1 ? (int)min<int64_t>(a.N - n, 8) : 0, v);
+      for (int p = 0; p < PA; ++p) *reinterpret_cast<vec8<MT>*>(&As[p][kk * kTP + mm]) = ta[p];
+      if (rows_sum) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) Bs[(nn + i) * kGP + kk] = v[i];
+        for (int i = 0; i < 8; ++i) rs[i] += va[i];
       }
     }
+    if (!b_n_unit) {
+      const int nn = tid >> 2, kk = (tid & 3) * 8;
+#pragma unroll
+      for (int p = 0; p < PB; ++p) *reinterpret_cast<vec8<MT>*>(&Bs[p][nn * kGP + kk]) = tb[p];
+    } else {
+      const int kk = tid >> 3, nn = (tid & 7) * 8;
+#pragma unroll
+      for (int p = 0; p < PB; ++p) *reinterpret_cast<vec8<MT>*>(&Bs[p][kk * kTP + nn]) = tb[p];
+    }
+  };
+  // Fragment i (rows 16 i .. of the wave's 32) of a plane stored as rows, or
+  // half i of the 32-row pair of a plane stored [k][row].
+  auto row_frag = [&](const MT* plane, int row0, int i) {
+    return *reinterpret_cast<const vec8<MT>*>(&plane[(row0 + i * 16 + i16) * kGP + 8 * g4]);
+  };
+  auto tr_frag = [&](const MT* plane, int row0, int i) {
+    const lds_v4s vl = (lds_v4s)&plane[(8 * g4 + (i16 >> 2)) * kTP + row0 + 8 * (i16 & 3)];
+    return vt_frag<MT, kTP>(vl, 0, i);
+  };
+  if (k0 < k1) load(k0);
+  for (int64_t kb = k0; kb < k1; kb += kGK) {
+    stage();
     __syncthreads();
-    vec8<float> af[2], bf[2];
+    if (kb + kGK < k1) load(kb + kGK);  // in flight during the products
+    vec8<MT> af[PA][2], bf[PB][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const float* pa = &As[(wm * 32 + i * 16 + i16) * kGP + 8 * g4];
-      const float* pb = &Bs[(wn * 32 + i * 16 + i16) * kGP + 8 * g4];
-      const float4 a0 = *reinterpret_cast<const float4*>(pa);
-      const float4 a1 = *reinterpret_cast<const float4*>(pa + 4);
-      const float4 b0 = *reinterpret_cast<const float4*>(pb);
-      const float4 b1 = *reinterpret_cast<const float4*>(pb + 4);
-      af[i] = vec8<float>{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      bf[i] = vec8<float>{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int p = 0; p < PA; ++p)
+        af[p][i] = a_k_unit ? row_frag(As[p], wm * 32, i) : tr_frag(As[p], wm * 32, i);
+#pragma unroll
+      for (int p = 0; p < PB; ++p)
+        bf[p][i] = b_n_unit ? tr_frag(Bs[p], wn * 32, i) : row_frag(Bs[p], wn * 32, i);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mma_16x16x32(af[i], bf[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (PB == 2) acc[i][j] = mma_16x16x32(af[0][i], bf[1][j], acc[i][j]);
+        if constexpr (PA == 2) acc[i][j] = mma_16x16x32(af[1][i], bf[0][j], acc[i][j]);
+        acc[i][j] = mma_16x16x32(af[0][i], bf[0][j], acc[i][j]);
+      }
     __syncthreads();
   }
   if (rows_sum) {
-    // Thread t staged rows 8 (t % 8) .. +7 at k = t / 8 of every step: sum the
-    // 32 threads of each row group through LDS (the last barrier ended every
-    // read of As).
+    // Thread t staged rows 8 (t % 8) .. +7 at k = t / 8 of every step: the 8
+    // lanes of a wave with the same t % 8 are summed by shuffles, then the 4
+    // waves through LDS (the last barrier ended every read of As).
 #pragma unroll
-    for (int i = 0; i < 8; ++i) As[(tid >> 3) * 64 + (tid & 7) * 8 + i] = rs[i];
-    __syncthreads();
-    if (tid < 64 && m0 + tid < a.M) {
-      float s = 0.f;
-      for (int q = 0; q < 32; ++q) s += As[q * 64 + tid];
-      atomicAdd(a.rowsum + m0 + tid, s);
+    for (int i = 0; i < 8; ++i) {
+      rs[i] += __shfl_xor(rs[i], 8);
+      rs[i] += __shfl_xor(rs[i], 16);
+      rs[i] += __shfl_xor(rs[i], 32);
     }
+    float* red = reinterpret_cast<float*>(&As[0][0]);
+    static_assert(sizeof(As) >= 4 * 64 * sizeof(float), "row-sum space");
+    if (lane < 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wave * 64 + lane * 8 + i] = rs[i];
+    }
+    __syncthreads();
+    if (tid < 64 && m0 + tid < a.M)
+      atomicAdd(a.rowsum + m0 + tid, red[tid] + red[64 + tid] + red[128 + tid] + red[192 + tid]);
   }
-  // Lane l holds column l % 16 of rows 4 (l / 16) .. +3 of each 16 x 16 tile.
+  // Lane l holds column l % 16 of rows 4 (l / 16) .. +3 of each 16 x 16 tile
+  // (fragment rows and columns; a transposed operand's are permuted).
   TC* C = static_cast<TC*>(a.C);
   const bool add_bias = a.bias && (!ATOMIC || blockIdx.z == 0);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 32 + j * 16 + i16;
+    const int n = n0 + wn * 32 + (b_n_unit ? 8 * (i16 >> 2) + 4 * j + (i16 & 3) : j * 16 + i16);
     if (n >= a.N) continue;
     const float bn = add_bias ? ld(static_cast<const TB*>(a.bias), n) : 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * 32 + i * 16 + 4 * g4 + r;
+        const int64_t m = m0 + wm * 32 + (a_k_unit ? i * 16 + 4 * g4 + r : 8 * g4 + 4 * i + r);
         if (m >= a.M) continue;
         const float v = acc[i][j][r] + bn;
         if constexpr (ATOMIC)
