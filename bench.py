@@ -416,8 +416,9 @@ def backward_flops_per_token(C, N):
 
 def backward_time(name, steps, warmup):
     """Sub-layer backward (swin_wmsa_bwd) on the workload's last block, timed
-    like a step.  Informational: float32 throughout, so its roofline is the
-    float32 matrix-core peak."""
+    like a step.  Informational; its rate is set against the float32
+    matrix-core peak, that of the attention backward's products (the GEMMs run
+    on the 16-bit matrix cores)."""
     import torch
     import shifted_window_attention_roll_amd as swin
     import workloads
@@ -451,7 +452,9 @@ def backward_time(name, steps, warmup):
     tf = T * backward_flops_per_token(case.C, case.M * case.M) / (ms * 1e-3) / 1e12
     del x, dy, ws, grads
     return {"bwd_ms": ms, "bwd_tokens_per_s": T / (ms * 1e-3), "bwd_tflops": tf,
-            "bwd_frac_of_fp32_mfma_peak": tf / PEAK_TFLOPS["fp32"], "compute": "fp32"}
+            "bwd_frac_of_fp32_mfma_peak": tf / PEAK_TFLOPS["fp32"],
+            "compute": "fp32 attention products; GEMMs on 16-bit matrix cores (exact, or "
+                       "operands as two bf16 terms), fp32 accumulation"}
 
 
 def fp8_time(name, steps, warmup):

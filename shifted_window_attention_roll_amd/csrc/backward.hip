@@ -471,15 +471,11 @@ __global__ __launch_bounds__(WV * 64) void attn_bwd_mfma_kernel(AttnBwd p) {
       }
   }
   __syncthreads();  // row max and inverse sum visible to the row group
-  // Phase 2: P, dP, D = rowsum(P dP); O = P V.
-  float dacc[TPW][4];  // the only per-row state held across chunks, with O
-  f32x4 o0[TPW], o1[TPW];
+  // Phase 2: P and O = P V; then D_i = sum_j P_ij dP_ij as dO_i . O_i (the
+  // same sum, since dP_ij = dO_i . V_j), without forming dP.
+  f32x4 o0[TPW], o1[TPW];  // the only per-row state held across chunks
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    o0[u] = o1[u] = zero4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dacc[u][r] = 0.f;
-  }
+  for (int u = 0; u < TPW; ++u) o0[u] = o1[u] = zero4;
 #pragma unroll 1
   for (int ch = 0; ch < NCH; ++ch) {
     if constexpr (NCH > 1) {
@@ -489,7 +485,7 @@ __global__ __launch_bounds__(WV * 64) void attn_bwd_mfma_kernel(AttnBwd p) {
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      const vec8<float> Qa = q_frag(u), DOa = do_frag(u);
+      const vec8<float> Qa = q_frag(u);
       float mr[4], ilr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -502,11 +498,9 @@ __global__ __launch_bounds__(WV * 64) void attn_bwd_mfma_kernel(AttnBwd p) {
         for (int tt = 0; tt < 2; ++tt) {
           const int kl = 32 * kb + 16 * tt + i16, key = ch * CH + kl;
           const f32x4 S = mma_16x16x32(Qa, frag_row(&b0[kl * LD + 8 * g4]), zero4);
-          const f32x4 dP = mma_16x16x32(DOa, frag_row(&b1[kl * LD + 8 * g4]), zero4);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float pv = __expf(logit(S[r], qrow_of(u, r), key) - mr[r]) * ilr[r];
-            dacc[u][r] = fmaf(pv, dP[r], dacc[u][r]);
             sw[(4 * g4 + r) * LD + 16 * tt + i16] = pv;
           }
         }
@@ -520,14 +514,22 @@ __global__ __launch_bounds__(WV * 64) void attn_bwd_mfma_kernel(AttnBwd p) {
   }
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dacc[u][r] += __shfl_xor(dacc[u][r], d);
+    // Lane: dims i16 and 16 + i16 of rows 4 g4 + r; D over the 16 lanes.
+    float dd[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int q = qrow_of(u, r);
-      if (i16 == 0) rd[q] = dacc[u][r];
+      const float* dr = dout + (base + (q < N ? q : 0)) * C;
+      dd[r] = q < N ? fmaf(dr[i16], o0[u][r], dr[16 + i16] * o1[u][r]) : 0.f;
+    }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dd[r] += __shfl_xor(dd[r], d);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = qrow_of(u, r);
+      if (i16 == 0) rd[q] = dd[r];
       if (q < N) {
         float* og = p.o + (base + q) * C + h * D;
         og[i16] = o0[u][r];
