@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
 // Per (window, head): recompute the attention and take its gradients, every
 // product on the float32 matrix cores.  Phases:
 //   1: row max m_i and sum l_i of exp(S_ij - m_i) over allowed keys;
-//   2: P, dP, D_i = sum_j P_ij dP_ij, O = P V (stored);
+//   2: P, O = P V (stored), then D_i = sum_j P_ij dP_ij as dO_i . O_i;
 //   3: dS = P (dP - D); table (and V2 tau) gradients; dQ = dS K;
 //   4: dV = P^T dO, dK = dS^T Q.
 // S_ij = c (q_i . k_j) + table[rel(i, j)], c = scale (V1) or 1 / max(tau,
@@ -281,7 +281,8 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, int64_t n) {
 //   S^T = K Q^T, dP^T = V dO^T, dV = P^T dO, dK = dS^T Q (phase 4).
 // LDS rows: K and V for phases 1-3, then Q and dO for phase 4, CH rows at a
 // time (all NP when they fit: windows up to 16; window 24 passes them in two
-// chunks per phase, each tile's state kept in registers across the chunks).
+// chunks per phase, the tiles' accumulators kept in registers across the
+// chunks and their row statistics in LDS).
 constexpr float kMasked = -1e30f;
 
 template <int NP, int WV, int CH, bool V2>
