@@ -39,3 +39,21 @@ def test_headline_is_the_largest_single_gpu_workload():
     flops = {n: bench.flops_per_token(w["C"], w["M"] ** 2) * w["B"] * w["H"] * w["W"] *
              len(w["shifts"]) for n, w in workloads.WORKLOADS.items()}
     assert bench.MAIN == max(flops, key=flops.get)
+
+
+def test_traffic_record_is_used_only_on_matching_sources(tmp_path, monkeypatch):
+    # A record taken on other kernel sources reads as unmeasured (None); one
+    # whose digest matches gives its bytes per launch.
+    import json
+    k, w = "fused_qkv_attn_kernel", "swinv2_g_stage1_384_w24_bf16"
+    digest = bench.source_digest(k)
+    (tmp_path / "profiles").mkdir()
+    rec = {"entries": {f"{w}:{k}": {"bytes_per_launch": 123.0, "source_digest": digest},
+                       f"{w}:proj_tiled_kernel": {"bytes_per_launch": 7.0,
+                                                  "source_digest": "0" * 16}}}
+    (tmp_path / "profiles" / "hbm_traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_digest", lambda kernel=None: digest)
+    assert bench.measured_traffic(k, w) == 123.0
+    assert bench.measured_traffic("proj_tiled_kernel", w) is None
+    assert bench.measured_traffic(k, "swin_b_stage3_b64_bf16") is None
