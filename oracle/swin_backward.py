@@ -43,13 +43,20 @@ from . import swin_oracle as so
 
 def wmsa_backward(x, w_qkv, b_qkv, w_proj, b_proj, bias_table, M: int, s: int, heads: int,
                   dy, mode: str = "v1", tau=None, scale: float | None = None,
-                  tau_min: float = 0.01, eps: float = 1e-12) -> dict:
+                  tau_min: float = 0.01, eps: float = 1e-12, windows=None) -> dict:
     """Gradients of L = sum(dy * wmsa_forward(...)).
 
     Returns a dict with dx [B,H,W,C], dw_qkv [3C,C], db_qkv [3C], dw_proj [C,C],
     db_proj [C], dtable [(2M-1)^2, heads] and (V2) dtau [heads], all float64.
     V2 also returns dtau_abs [heads]: the same sum over |terms|, which measures
     how far the signed sum cancels (an error scale for dtau, not a gradient).
+
+    windows: optional window indices (0 .. B nW - 1, window order).  Every
+    window's part of dx depends only on that window's tokens, so the same
+    steps run on those windows alone; the result then holds dxw [len, N, C]
+    (the gradient of their slots, mapped to tokens by
+    ``swin_oracle.window_token_source``) in place of dx, and the other entries
+    sum over those windows only.
     """
     x = np.asarray(x, np.float64)
     dy = np.asarray(dy, np.float64)
@@ -70,6 +77,8 @@ def wmsa_backward(x, w_qkv, b_qkv, w_proj, b_proj, bias_table, M: int, s: int, h
 
     # ---- forward, keeping what the backward needs ------------------------
     xw = so.partition_shift(x, M, s)                      # [nw, N, C]
+    widx = np.arange(xw.shape[0]) if windows is None else np.asarray(windows, np.int64)
+    xw = xw[widx]
     nw = xw.shape[0]
     qkv = xw @ w_qkv.T + b_qkv
     q = qkv[:, :, 0 * C:1 * C].reshape(nw, N, heads, d).transpose(0, 2, 1, 3)
@@ -94,7 +103,7 @@ def wmsa_backward(x, w_qkv, b_qkv, w_proj, b_proj, bias_table, M: int, s: int, h
     region = so.region_labels(H, W, M, s)
     allowed = np.ones((nw, 1, N, N), bool)
     if s > 0:
-        allowed = (region[:, :, None] == region[:, None, :])[np.arange(nw) % nW][:, None]
+        allowed = (region[:, :, None] == region[:, None, :])[widx % nW][:, None]
     logits = np.where(allowed, logits, -np.inf)
     p = np.exp(logits - logits.max(axis=-1, keepdims=True))
     p = p / p.sum(axis=-1, keepdims=True)
@@ -103,7 +112,7 @@ def wmsa_backward(x, w_qkv, b_qkv, w_proj, b_proj, bias_table, M: int, s: int, h
     # ---- backward ------------------------------------------------------------
     # Output projection y_w = o Wp^T + bp, then the inverse shift: its adjoint is
     # the forward map applied to dy.
-    dyw = so.partition_shift(dy, M, s)                    # [nw, N, C]
+    dyw = so.partition_shift(dy, M, s)[widx]              # [nw, N, C]
     db_proj = dyw.sum(axis=(0, 1))
     dw_proj = dyw.reshape(-1, C).T @ o.reshape(-1, C)
     do = (dyw @ w_proj).reshape(nw, N, heads, d).transpose(0, 2, 1, 3)
@@ -145,10 +154,12 @@ def wmsa_backward(x, w_qkv, b_qkv, w_proj, b_proj, bias_table, M: int, s: int, h
     db_qkv = dqkv.sum(axis=(0, 1))
     dw_qkv = dqkv.reshape(-1, 3 * C).T @ xw.reshape(-1, C)
     dxw = dqkv @ w_qkv
+    out.update(dw_qkv=dw_qkv, db_qkv=db_qkv, dw_proj=dw_proj, db_proj=db_proj, dtable=dtable)
+    if windows is not None:
+        out["dxw"] = dxw
+        return out
     # The forward map's adjoint is the inverse map (a permutation of tokens).
-    dx = so.reverse_unshift(dxw, B, H, W, M, s)
-    out.update(dx=dx, dw_qkv=dw_qkv, db_qkv=db_qkv, dw_proj=dw_proj, db_proj=db_proj,
-               dtable=dtable)
+    out["dx"] = so.reverse_unshift(dxw, B, H, W, M, s)
     return out
 
 

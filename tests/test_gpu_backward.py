@@ -199,3 +199,52 @@ def test_backward_large_bias(gpu):
                             workloads.f64(blk.b_proj), workloads.f64(blk.table), 8, 4, 2,
                             workloads.f64(dy), "v1")
     _assert_grads(g, ref, "fp32", "v1", "large bias")
+
+
+def test_backward_full_size_sampled_windows(gpu):
+    # SwinV2-G stage 1 (384 x 384, C 512, 16 heads, window 24, shift 12,
+    # bfloat16) as the bench times it: dx of five windows (first, interior,
+    # last-column, last-row and corner; the last three masked) against the
+    # oracle run on those windows alone, every element of dx finite, and the
+    # closed forms that hold at any size: db_proj is the sum of dy, and each
+    # head's table gradient sums to zero.
+    from oracle import swin_oracle as so
+    name = "swinv2_g_stage1_384_w24_bf16"
+    _say(f"bwd full size {name}")
+    swin = gpu
+    case = workloads.make_workload(name)
+    blk = case.blocks[-1]
+    M, s, heads, C = case.M, blk.s, case.heads, case.C
+    dy = workloads.make_upstream_grad(case.x.shape, case.dtype, 3)
+    dev = "cuda"
+    g = swin.wmsa_bwd(case.x.to(dev), blk.w_qkv.to(dev), blk.b_qkv.to(dev), blk.w_proj.to(dev),
+                      helpers.gpu_table(case, blk, dev), dy.to(dev), M, s, heads, case.mode,
+                      tau=None if blk.tau is None else blk.tau.to(dev))
+    torch.cuda.synchronize()
+    dx = g["dx"].float().cpu()
+    assert torch.isfinite(dx).all()
+    nwx = case.W // M
+    windows = [0, 5 * nwx + 7, 9 * nwx + nwx - 1, (case.H // M - 1) * nwx + 3,
+               (case.H // M) * nwx - 1]
+    ref = sbw.wmsa_backward(workloads.f64(case.x), workloads.f64(blk.w_qkv),
+                            workloads.f64(blk.b_qkv), workloads.f64(blk.w_proj),
+                            workloads.f64(blk.b_proj), helpers.oracle_table(case, blk), M, s,
+                            heads, workloads.f64(dy), case.mode,
+                            tau=None if blk.tau is None else workloads.f64(blk.tau),
+                            windows=windows)
+    src = so.window_token_source(case.B, case.H, case.W, M, s)[windows]   # [5, N]
+    got = workloads.f64(dx).reshape(-1, C)[src]
+    r = ref["dxw"]
+    scale = float(np.abs(r).max())
+    err = np.abs(got - r)
+    bound = TOL * scale + ULP[case.dtype] * np.abs(r)
+    rel = float(np.linalg.norm(got - r) / np.linalg.norm(r))
+    _say(f"  dx on {len(windows)} windows: max err {err.max():.3g} (scale {scale:.3g}), "
+         f"rel-L2 {rel:.3g}")
+    assert float((err - bound).max()) <= 0
+    assert rel <= TOL + 2 * ULP[case.dtype]
+    dbp = g["db_proj"].cpu().double().numpy()
+    dbp_ref = workloads.f64(dy).reshape(-1, C).sum(axis=0)
+    assert np.abs(dbp - dbp_ref).max() <= TOL * np.abs(dbp_ref).max()
+    dt = g["dtable"].cpu().double().numpy()
+    assert (np.abs(dt.sum(axis=0)) <= TOL * np.abs(dt).sum(axis=0)).all()

@@ -151,3 +151,27 @@ def test_cpb_backward_finite_differences():
             lm = L()
             arr[i] = keep
             assert abs((lp - lm) / 2e-6 - g[key][i]) <= 1e-6 * max(1.0, abs(g[key][i])), (key, i)
+
+
+@pytest.mark.parametrize("mode,s", [("v1", 2), ("v2", 2), ("v1", 0)])
+def test_window_subset_matches_whole_image(mode, s):
+    # A window subset gives the whole image's dx at its windows' tokens, and
+    # the partial sums of two complementary subsets add up to the whole
+    # image's gradients (windows are independent given the weights).
+    M, heads = 4, 2
+    p, dy = _case(12, 2, 8, 12, 16, heads, M, mode, tau=[0.3, 0.02])
+    args = (p["x"], p["w_qkv"], p["b_qkv"], p["w_proj"], p["b_proj"], p["table"], M, s, heads,
+            dy, mode)
+    full = sbw.wmsa_backward(*args, tau=p.get("tau"))
+    nwin = 2 * (8 // M) * (12 // M)
+    a = [0, 3, 5, nwin - 1]                # includes masked (last row / column) windows
+    b = [w for w in range(nwin) if w not in a]
+    ga = sbw.wmsa_backward(*args, tau=p.get("tau"), windows=a)
+    gb = sbw.wmsa_backward(*args, tau=p.get("tau"), windows=b)
+    src = so.window_token_source(2, 8, 12, M, s)          # [windows, N] flat token
+    dx_flat = full["dx"].reshape(-1, 16)
+    np.testing.assert_allclose(ga["dxw"], dx_flat[src[a]], rtol=1e-12, atol=1e-12)
+    for k in ("dw_qkv", "db_qkv", "dw_proj", "db_proj", "dtable") + (("dtau",) if mode == "v2"
+                                                                     else ()):
+        np.testing.assert_allclose(ga[k] + gb[k], full[k], rtol=1e-10, atol=1e-10)
+    assert "dx" not in ga
