@@ -91,6 +91,42 @@ def test_block_swin_t_stage1_sampled(gpu):
     _assert_block_close(got, ref, "fp16", "block sampled")
 
 
+@pytest.mark.parametrize("name,n_random", [
+    ("swin_b_stage3_b64_bf16", 12),          # C = 512: MLP on the tiled dense GEMMs
+    ("swinv2_b_stage1_w16_bf16", 12),        # C = 128: the fused MLP, window-16 block kernel
+    ("swinv2_g_stage1_384_w24_bf16", 6),     # C = 512, window 24, hidden 2048
+])
+def test_block_workload_sampled(gpu, name, n_random):
+    # The full block on the workload's last block with the MLP weights the
+    # bench times it with: sampled windows (first, last, the masked last row /
+    # column and a seeded handful) against the oracle run on those windows.
+    _say(f"block {name} sampled")
+    case = workloads.make_workload(name)
+    blk = case.blocks[-1]
+    M, s, heads, C = case.M, blk.s, case.heads, case.C
+    extra = workloads.make_block_params(C, case.dtype, 77, fc_std=0.02)
+    dev = "cuda"
+    gp = {"w_qkv": blk.w_qkv.to(dev), "b_qkv": blk.b_qkv.to(dev), "w_proj": blk.w_proj.to(dev),
+          "b_proj": blk.b_proj.to(dev), "table": helpers.gpu_table(case, blk, dev)}
+    op = {"w_qkv": workloads.f64(blk.w_qkv), "b_qkv": workloads.f64(blk.b_qkv),
+          "w_proj": workloads.f64(blk.w_proj), "b_proj": workloads.f64(blk.b_proj),
+          "table": helpers.oracle_table(case, blk)}
+    if blk.tau is not None:
+        gp["tau"] = blk.tau.to(dev)
+        op["tau"] = workloads.f64(blk.tau)
+    gp.update({k: v.to(dev) for k, v in extra.items()})
+    op.update({k: workloads.f64(v) for k, v in extra.items()})
+    x = case.x.to(dev)
+    out = torch.full_like(x, float("nan"))
+    y = gpu.block_fwd(x, gp, M, s, heads, case.mode, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+    wins = helpers.sample_windows(case.B, case.H, case.W, M, n_random, seed=11)
+    tok, ref = sb.block_forward(workloads.f64(case.x), op, M, s, heads, case.mode, windows=wins)
+    got = workloads.f64(y.cpu()).reshape(-1, C)[tok]
+    _assert_block_close(got, ref, case.dtype, f"block {name} sampled")
+
+
 def test_block_deterministic_and_written(gpu):
     case, blk, gp, op = _setup(2, 16, 16, 128, 4, 8, 4, "bf16", "v2", seed=99)
     x = case.x.cuda()
